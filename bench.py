@@ -1,0 +1,187 @@
+"""Throughput of the block-scaled FP8 hot path on one MI355X.
+
+One step = one pass of the whole path over the prefill-shaped linear layer:
+
+  1. act_quant (ue8m0 scales) of bf16 activations [8192, 7168]
+     (the act_quant bandwidth workload's shape, 0.1% outliers x100);
+  2. weight_dequant of the E4M3 weight [18432, 7168] with its [144, 56]
+     block scales to bf16 (the dequant bandwidth workload);
+  3. fp8_block_gemm of the quantized activations with that weight, bf16 out
+     (the prefill GEMM, 8192 x 18432 x 7168).
+
+``value`` = 2*M*N*K / step time (TFLOP/s of the whole step, inputs resident
+in HBM).  Per-kernel times come from HIP events recorded on the stream the
+kernels run on; the GEMM is the dominant kernel and its roofline is the dense
+FP8 MFMA peak.  Each step touches about 1 GB, well beyond the 256 MB Infinity
+Cache, so every kernel reads its inputs from HBM.
+
+``cpu_baseline`` times the CPU oracle (test infrastructure, never tuned) on a
+bounded sample of the same workload: the first ``--cpu-rows`` activation rows
+through act_quant and the GEMM, and the matching fraction of the weight through
+weight_dequant.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, N, K = 8192, 18432, 7168
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+
+# algorithmic bytes per launch (what the method must move)
+ACT_QUANT_BYTES = M * K * 2 + M * K + M * (K // 128) * 4                 # 177,995,776
+DEQUANT_BYTES = N * K + (N // 128) * (K // 128) * 4 + N * K * 2          # 396,393,984 incl. scales
+GEMM_FLOP = 2 * M * N * K                                                # 2,164,663,517,184
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--cpu-rows", type=int, default=512,
+                   help="activation rows in the CPU oracle sample (0 skips it)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+def cpu_baseline(x_bf16, w, ws, rows):
+    """Time the oracle on the first `rows` rows (and rows/M of the weight)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    x = x_bf16[:rows].float().numpy()
+    wrows = max(128, (N * rows // M) // 128 * 128)
+    t0 = time.perf_counter()
+    a, a_s = oracle.act_quant(x, 128, "ue8m0")
+    oracle.weight_dequant(w[:wrows], np.ascontiguousarray(ws[:wrows // 128]), 128, "bf16")
+    oracle.fp8_gemm(a, a_s, w, ws)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * N * K
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads if blas_threads else cores,
+        "kind": "oracle",
+        "sample": (f"first {rows} of {M} activation rows through act_quant(ue8m0) + fp8_gemm "
+                   f"(all {N} columns) and {wrows} of {N} weight rows through weight_dequant; "
+                   f"{dt:.2f} s; value = 2*{rows}*N*K / time; host has {cores} usable cores"),
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every kernel here runs on a single device with no cross-GPU work).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_quant_amd as fb
+    from inputs import gen
+
+    dev = torch.device("cuda:0")
+    fb.load_library()
+
+    d = gen.prefill_gemm(1)
+    x_cpu, w_np, ws_np = d["x"], d["w"], d["w_s"]
+    x = x_cpu.to(dev)
+    w = torch.from_numpy(w_np).to(dev).view(torch.float8_e4m3fn)
+    ws = torch.from_numpy(ws_np).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        y, s = fb.act_quant(x, 128, "ue8m0")
+        if ev is not None:
+            ev[1].record(stream)
+        wd = fb.weight_dequant(w, ws, 128, torch.bfloat16)
+        if ev is not None:
+            ev[2].record(stream)
+        c = fb.fp8_gemm(y, s, w, ws, torch.bfloat16)
+        if ev is not None:
+            ev[3].record(stream)
+        return c, wd
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronized on both sides
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    aq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dq_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    gemm_tflops = GEMM_FLOP / (gm_ms * 1e-3) / 1e12
+    aq_gbs = ACT_QUANT_BYTES / (aq_ms * 1e-3) / 1e9
+    dq_gbs = DEQUANT_BYTES / (dq_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak); act_quant/dequant HBM GB/s",
+        "value": GEMM_FLOP / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": ("prefill linear layer: act_quant ue8m0 of bf16 [8192,7168] + weight_dequant "
+                         "[18432,7168]->bf16 + block-scaled FP8 GEMM 8192x18432x7168, bf16 out"),
+            "m": M, "n": N, "k": K, "scale_fmt": "ue8m0", "out": "bf16",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": gemm_tflops,
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / PEAK_FP8_TFLOPS,
+            "traffic": None,
+        },
+        "kernels": {
+            "act_quant": {"us": aq_ms * 1e3, "GB/s": aq_gbs, "frac_hbm": aq_gbs / PEAK_HBM_GBS,
+                          "bytes": ACT_QUANT_BYTES},
+            "weight_dequant": {"us": dq_ms * 1e3, "GB/s": dq_gbs, "frac_hbm": dq_gbs / PEAK_HBM_GBS,
+                               "bytes": DEQUANT_BYTES},
+            "block_gemm": {"us": gm_ms * 1e3, "TFLOP/s": gemm_tflops,
+                           "frac_mfma": gemm_tflops / PEAK_FP8_TFLOPS, "flop": GEMM_FLOP},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu and args.cpu_rows > 0:
+        result["cpu_baseline"] = cpu_baseline(x_cpu, w_np, ws_np, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+"""Block-scaled FP8 (E4M3) quantization and GEMM on AMD Instinct MI355X.
+
+A thin ctypes binding over the C ABI of ``libfp8bsq.so`` (declared in
+``include/fp8bsq.h``).  PyTorch supplies device memory and the current stream;
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is not built, or a tensor is not on a GPU, the calls
+raise.
+
+Functions follow the call shapes the pages give:
+
+* ``act_quant(x, block_size=128, scale_fmt=None) -> (y, s)``
+* ``weight_dequant(x, s, block_size=128, out_dtype=torch.float32) -> y``
+* ``fp8_gemm(a, a_s, b, b_s, out_dtype=torch.bfloat16) -> c``
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = ["act_quant", "weight_dequant", "fp8_gemm", "Fp8Error", "library_path", "load_library"]
+
+Fp8Error = _lib.Fp8Error
+library_path = _lib.library_path
+load_library = _lib.load_library
+
+_DTYPE = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+_SCALE_FMT = {None: _lib.SCALE_NONE, "ue8m0": _lib.SCALE_UE8M0}
+
+
+def _stream_handle(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("fp8_block_scaled_quant_amd runs on the GPU only: tensor is on " + str(t.device))
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dev = ts[0].device
+    if any(t.device != dev for t in ts):
+        raise ValueError("all tensors must be on the same device")
+
+
+def _codes(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype == torch.uint8:
+        return t
+    raise TypeError("E4M3 operands must be torch.float8_e4m3fn (or uint8 codes)")
+
+
+def act_quant(x: torch.Tensor, block_size: int = 128, scale_fmt=None):
+    """Dynamic activation quantization: one FP32 scale per 1 x block_size block.
+
+    ``x`` is a contiguous bf16 or fp32 CUDA tensor whose last dimension is a
+    multiple of ``block_size``.  Returns ``y`` (float8_e4m3fn, x's shape) and
+    ``s`` (float32, ``x.shape[:-1] + (K // block_size,)``).
+    """
+    _require_gpu(x)
+    if x.dtype not in _DTYPE:
+        raise TypeError("act_quant takes bf16 or fp32 input")
+    if scale_fmt not in _SCALE_FMT:
+        raise ValueError(f"unknown scale_fmt {scale_fmt!r}")
+    k = x.shape[-1]
+    if k % block_size != 0:
+        raise ValueError("last dimension must be a multiple of block_size")
+    rows = x.numel() // k if k else 0
+    y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty(x.shape[:-1] + (k // block_size,), dtype=torch.float32, device=x.device)
+    if rows:
+        _lib.check(_lib.lib().fp8_act_quant(
+            ctypes.c_void_p(x.data_ptr()), _DTYPE[x.dtype], rows, k, block_size,
+            _SCALE_FMT[scale_fmt], ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+            _stream_handle(x)))
+    return y.view(torch.float8_e4m3fn), s
+
+
+def weight_dequant(x: torch.Tensor, s: torch.Tensor, block_size: int = 128,
+                   out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Dequantize a 2-D E4M3 weight with its [ceil(M/bs), ceil(N/bs)] FP32 block scales."""
+    x = _codes(x)
+    _require_gpu(x, s)
+    if x.dim() != 2:
+        raise ValueError("weight must be 2-D")
+    if s.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    if out_dtype not in _DTYPE:
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    m, n = x.shape
+    grid = (-(-m // block_size), -(-n // block_size))
+    if tuple(s.shape) != grid:
+        raise ValueError(f"scale grid must be {grid}, got {tuple(s.shape)}")
+    y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    if m and n:
+        _lib.check(_lib.lib().fp8_weight_dequant(
+            ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(s.data_ptr()), m, n, block_size,
+            ctypes.c_void_p(y.data_ptr()), _DTYPE[out_dtype], _stream_handle(x)))
+    return y
+
+
+def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+             out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Block-scaled FP8 GEMM ``C = A . B^T`` (B is the [out, in] weight).
+
+    ``a`` [..., K] E4M3 with ``a_s`` [..., K/128]; ``b`` [N, K] E4M3 with
+    ``b_s`` [ceil(N/128), K/128].  Returns ``[..., N]`` in ``out_dtype``.
+    """
+    a, b = _codes(a), _codes(b)
+    _require_gpu(a, a_s, b, b_s)
+    if a_s.dtype != torch.float32 or b_s.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    if out_dtype not in _DTYPE:
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    k = a.shape[-1]
+    if b.dim() != 2 or b.shape[1] != k:
+        raise ValueError("b must be [N, K] with A's K")
+    if k % 128 != 0:
+        raise ValueError("K must be a multiple of 128")
+    m = a.numel() // k if k else 0
+    n = b.shape[0]
+    if tuple(a_s.shape) != tuple(a.shape[:-1]) + (k // 128,):
+        raise ValueError("a_s must be a.shape[:-1] + (K/128,)")
+    if tuple(b_s.shape) != (-(-n // 128), k // 128):
+        raise ValueError("b_s must be [ceil(N/128), K/128]")
+    c = torch.empty(tuple(a.shape[:-1]) + (n,), dtype=out_dtype, device=a.device)
+    if m and n:
+        _lib.check(_lib.lib().fp8_block_gemm(
+            ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(a_s.data_ptr()),
+            ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),
+            ctypes.c_void_p(c.data_ptr()), _DTYPE[out_dtype], m, n, k, _stream_handle(a)))
+    return c

@@ -1,0 +1,79 @@
+// C ABI of the block-scaled FP8 library: argument validation and dispatch.
+// Every check runs before any HIP call, so a rejected call queues nothing.
+#include <stdint.h>
+
+#include "fp8bsq.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;        // per-dimension limit of the launch grids
+constexpr int64_t kMaxGemmRows = (int64_t)65535 * 64; // grid.y limit of the GEMM launch
+
+bool aligned(const void *p, uintptr_t bytes) { return ((uintptr_t)p % bytes) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FP8BSQ_OK : FP8BSQ_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8_act_quant(const void *x, int x_dtype, int64_t rows, int64_t k, int block_size,
+                  int scale_fmt, uint8_t *y, float *s, void *hip_stream) {
+  if (!x || !y || !s) return FP8BSQ_EINVAL;
+  if (rows <= 0 || k <= 0) return FP8BSQ_EINVAL;
+  if (x_dtype != FP8BSQ_F32 && x_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
+  if (scale_fmt != FP8BSQ_SCALE_NONE && scale_fmt != FP8BSQ_SCALE_UE8M0) return FP8BSQ_EINVAL;
+  if (block_size != 128) return FP8BSQ_EUNSUPPORTED;
+  if (k % block_size != 0) return FP8BSQ_ESHAPE;
+  if (!aligned(x, 16) || !aligned(y, 8) || !aligned(s, 4)) return FP8BSQ_EALIGN;
+  if (rows >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
+  const int64_t nblocks = rows * (k / block_size);
+  if ((nblocks + 63) / 64 >= kMaxDim) return FP8BSQ_ERANGE;
+  return launch_status(fp8bsq::launch_act_quant(x, x_dtype == FP8BSQ_BF16, nblocks,
+                                                scale_fmt == FP8BSQ_SCALE_UE8M0, y, s,
+                                                (hipStream_t)hip_stream));
+}
+
+int fp8_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, int block_size,
+                       void *y, int y_dtype, void *hip_stream) {
+  if (!x || !s || !y) return FP8BSQ_EINVAL;
+  if (m <= 0 || n <= 0) return FP8BSQ_EINVAL;
+  if (y_dtype != FP8BSQ_F32 && y_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
+  if (block_size != 128) return FP8BSQ_EUNSUPPORTED;
+  if (!aligned(s, 4) || !aligned(y, y_dtype == FP8BSQ_F32 ? 4 : 2)) return FP8BSQ_EALIGN;
+  if (m >= kMaxDim || n >= kMaxDim || m * n >= ((int64_t)1 << 50)) return FP8BSQ_ERANGE;
+  return launch_status(fp8bsq::launch_weight_dequant(x, s, m, n, y, y_dtype == FP8BSQ_BF16,
+                                                     (hipStream_t)hip_stream));
+}
+
+int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
+                   void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
+  if (!a || !a_s || !b || !b_s || !c) return FP8BSQ_EINVAL;
+  if (m <= 0 || n <= 0 || k <= 0) return FP8BSQ_EINVAL;
+  if (c_dtype != FP8BSQ_F32 && c_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
+  if (k % 128 != 0) return FP8BSQ_ESHAPE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
+      !aligned(c, 4))
+    return FP8BSQ_EALIGN;
+  if (m > kMaxGemmRows || n >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
+  return launch_status(fp8bsq::launch_block_gemm(a, a_s, b, b_s, c, c_dtype == FP8BSQ_BF16, m, n,
+                                                 k, (hipStream_t)hip_stream));
+}
+
+const char *fp8bsq_strerror(int status) {
+  switch (status) {
+    case FP8BSQ_OK: return "ok";
+    case FP8BSQ_EINVAL: return "invalid argument (null pointer, non-positive size or unknown enum)";
+    case FP8BSQ_ESHAPE: return "a dimension that must be a multiple of the block size is not";
+    case FP8BSQ_EUNSUPPORTED: return "unsupported block size (only 128 is implemented)";
+    case FP8BSQ_EALIGN: return "pointer is not aligned as the entry point requires";
+    case FP8BSQ_ELAUNCH: return "HIP runtime error at kernel launch";
+    case FP8BSQ_ERANGE: return "size exceeds the kernels' indexing limits";
+    default: return "unknown status";
+  }
+}
+
+const char *fp8bsq_version(void) { return "0.1.0"; }
+
+}  // extern "C"

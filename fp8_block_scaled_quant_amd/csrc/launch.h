@@ -1,0 +1,24 @@
+// Internal launchers: one per kernel family.  Arguments are already validated
+// by the C ABI layer (abi.cpp); each returns the HIP error of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bsq {
+
+// x: [nblocks, 128] bf16 or fp32 (16-byte aligned); y: [nblocks, 128] codes;
+// s: [nblocks] scales.
+hipError_t launch_act_quant(const void *x, bool x_bf16, int64_t nblocks, bool ue8m0, uint8_t *y,
+                            float *s, hipStream_t stream);
+
+// x: [m, n] codes; s: [ceil(m/128), ceil(n/128)]; y: [m, n] fp32 or bf16.
+hipError_t launch_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, void *y,
+                                 bool y_bf16, hipStream_t stream);
+
+// C[m, n] = block-scaled A[m, k] . B[n, k]^T.
+hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
+                             const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                             int64_t k, hipStream_t stream);
+
+}  // namespace fp8bsq

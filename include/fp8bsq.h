@@ -1,0 +1,138 @@
+/*
+ * fp8bsq.h -- C ABI of the block-scaled FP8 library for AMD Instinct MI355X
+ * (gfx950): dynamic 1x128 activation quantization, 128x128 block-scaled
+ * weight dequantization, and the block-scaled FP8 E4M3 GEMM those two feed.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer (hipMalloc'd or a PyTorch CUDA
+ *    tensor's data_ptr) owned by the caller, who keeps it alive until the work
+ *    queued on `hip_stream` has finished.  The library allocates nothing and
+ *    keeps no state between calls; calls are re-entrant and thread-safe.
+ *  - All tensors are dense and row-major.  E4M3 codes are bytes in the OCP
+ *    E4M3FN encoding (PyTorch's torch.float8_e4m3fn).  Scales are FP32.
+ *  - Work is queued on `hip_stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronizing.
+ *  - The return value is FP8BSQ_OK or an fp8bsq_status code.  Arguments are
+ *    validated before any HIP call; on a validation error nothing is queued.
+ *    FP8BSQ_ELAUNCH reports an error from the HIP runtime after the launch.
+ *  - Inputs must be finite.  NaN/Inf inputs or scales give unspecified (but
+ *    memory-safe) outputs.
+ *  - block_size is an argument because the format makes it configurable; only
+ *    128 is implemented (FP8BSQ_EUNSUPPORTED otherwise).
+ *
+ * Citations name the web page and the section the operation is defined in.
+ */
+#ifndef FP8BSQ_H
+#define FP8BSQ_H
+
+#include <stdint.h>
+
+#define FP8BSQ_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BSQ_OK = 0,
+  FP8BSQ_EINVAL = 1,       /* null pointer, dimension <= 0, unknown enum value */
+  FP8BSQ_ESHAPE = 2,       /* a dimension that must be a multiple of block_size is not */
+  FP8BSQ_EUNSUPPORTED = 3, /* block_size != 128 */
+  FP8BSQ_EALIGN = 4,       /* a pointer lacks the alignment stated for it */
+  FP8BSQ_ELAUNCH = 5,      /* the HIP runtime reported an error for the launch */
+  FP8BSQ_ERANGE = 6        /* a size does not fit the kernels' 32-bit indexing limits */
+} fp8bsq_status;
+
+typedef enum { FP8BSQ_F32 = 0, FP8BSQ_BF16 = 1 } fp8bsq_dtype;
+
+typedef enum {
+  FP8BSQ_SCALE_NONE = 0,  /* scale_fmt=None: s = fl32(amax / 448) */
+  FP8BSQ_SCALE_UE8M0 = 1  /* scale_fmt="ue8m0": s rounded up to a power of two */
+} fp8bsq_scale_fmt;
+
+/*
+ * fp8_act_quant -- dynamic activation quantization, one scale per 1 x 128 block.
+ *
+ * Defined on the page "Understanding Dynamic and Static Activation
+ * Quantization Schemes in DeepSeek-V3", section "How Dynamic Activation
+ * Quantization Works" (act_quant(x, block_size=128, scale_fmt=None) -> (y, s)),
+ * and on "DeepSeek-V3 quantization_config Parameters Explained", section "The
+ * activation_scheme Parameter": per block, amax = max |x| clamped to at least
+ * 1e-4, s = amax / 448, y = x / s in E4M3.
+ *
+ *   x          [rows, k] activations, dtype x_dtype (FP8BSQ_F32 or FP8BSQ_BF16),
+ *              16-byte aligned.
+ *   rows, k    rows >= 1, k >= 1 and k % block_size == 0 (else FP8BSQ_ESHAPE).
+ *   scale_fmt  FP8BSQ_SCALE_NONE or FP8BSQ_SCALE_UE8M0 (smallest power of two
+ *              >= fl32(amax/448)).
+ *   y          [rows, k] E4M3 codes out, 8-byte aligned:
+ *              y = RNE_E4M3(fl32(x / s)), saturating at +-448, sign kept on zero.
+ *   s          [rows, k / block_size] FP32 scales out, 4-byte aligned.
+ *
+ * Results are bit-identical to the CPU oracle for finite x.
+ */
+FP8BSQ_API int fp8_act_quant(const void *x, int x_dtype, int64_t rows, int64_t k, int block_size,
+                  int scale_fmt, uint8_t *y, float *s, void *hip_stream);
+
+/*
+ * fp8_weight_dequant -- 128x128 block-scaled weight dequantization.
+ *
+ * Defined on the page "How weight_dequant Handles Per-Block Scaling in
+ * DeepSeek-V3 FP8 GEMM", sections "Per-Block Scaling Architecture", "Grid
+ * Mapping and Scale Lookup" and "Dequantization Computation": each
+ * block_size x block_size tile of x is converted to FP32 and multiplied by its
+ * own scale, y = x * s; edge tiles are masked.
+ *
+ *   x        [m, n] E4M3 codes (m weight rows, n columns), any alignment.
+ *   s        [ceil(m / block_size), ceil(n / block_size)] FP32 scales
+ *            (weight_scale_inv), row-major: tile (i, j) at i * ceil(n/bs) + j.
+ *   m, n     >= 1; need not be multiples of block_size.
+ *   y        [m, n] out, dtype y_dtype: FP8BSQ_F32 gives fl32(DEC(x) * s);
+ *            FP8BSQ_BF16 gives that product rounded to nearest even bf16.
+ *
+ * Results are bit-identical to the CPU oracle for finite scales.  Inputs with
+ * n % 16 == 0 and 16-byte-aligned x and y take the vectorized path.
+ */
+FP8BSQ_API int fp8_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, int block_size,
+                       void *y, int y_dtype, void *hip_stream);
+
+/*
+ * fp8_block_gemm -- block-scaled FP8 GEMM, C = A . B^T.
+ *
+ * Defined on the page "How weight_dequant Handles Per-Block Scaling in
+ * DeepSeek-V3 FP8 GEMM", section "Relationship to FP8 GEMM Operations"
+ * (fp8_gemm(a, a_s, b, b_s): the per-block scales are applied inside the
+ * product, no dequantized weight is materialized), with the weight used as in
+ * F.linear(x, W) ("Practical Usage Example"), and on the page "DeepSeek-V3:
+ * How Selective FP8 Stays Stable" ("Learning outcomes", FAQ and "Lower
+ * precision is a constrained budget"): partial sums are promoted to FP32
+ * periodically and outputs are BF16 or FP32.  Here the promotion happens once
+ * per 128-wide K block: for each K block kb,
+ *     C[i, j] += (sum_{k in kb} A[i, k] * B[j, k]) * a_s[i, kb] * b_s[j / 128, kb].
+ *
+ *   a      [m, k] E4M3 activation codes (act_quant's y), 16-byte aligned.
+ *   a_s    [m, k / 128] FP32 activation scales (act_quant's s).
+ *   b      [n, k] E4M3 weight codes ([out, in]), 16-byte aligned.
+ *   b_s    [ceil(n / 128), k / 128] FP32 weight block scales.
+ *   c      [m, n] out, dtype c_dtype (FP8BSQ_F32 or FP8BSQ_BF16, RNE from the
+ *          FP32 accumulator); 4-byte aligned.
+ *   m, n   >= 1; k >= 128 and k % 128 == 0 (else FP8BSQ_ESHAPE).
+ *
+ * Accumulation order is not specified; every element is within
+ * 1e-3 * sum_k |a_k * b_k| of the exact result (plus one bf16 ulp for BF16).
+ */
+FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
+                   void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream);
+
+/* Short English text for a status code; never NULL. */
+FP8BSQ_API const char *fp8bsq_strerror(int status);
+
+/* Library version, "major.minor.patch". */
+FP8BSQ_API const char *fp8bsq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BSQ_H */
