@@ -105,11 +105,215 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Tiled kernel for large M.
+//
+// Workgroup tile 256 (M) x 128 (N), 512 threads = 8 waves arranged 4 x 2, each
+// wave a 64 x 64 output tile (4 x 4 MFMA tiles).  Per 128-wide K block the
+// workgroup stages A[256 x 128] and B[128 x 128] (48 KiB of E4M3 codes) in LDS,
+// double-buffered: the global loads for block kb+1 are issued into registers
+// before block kb is computed and written to the other LDS buffer after it, so
+// one barrier per K block suffices.  A 128-column N tile lies inside one
+// 128-row weight block, so b_s is one scalar per K block.  Activation scales
+// are staged eight K blocks at a time, transposed to [kb][row] so a lane reads
+// the four rows it owns in one 16-byte LDS read.
+//
+// LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r is stored at
+// chunk c ^ swz(r), which spreads the 16 rows a fragment read touches over all
+// banks.
+//
+// Tile order is XCD-aware: workgroup ids are dealt round-robin to the eight
+// XCDs, so consecutive tiles of the grouped raster order (4 M tiles by the N
+// tiles) are given to ids of the same XCD and share its L2.
+// ---------------------------------------------------------------------------
+constexpr int kTileM = 256, kTileN = 128, kThreads = 512, kScaleGroup = 8;
+
+struct TileSmem {
+  uint8_t a[2][kTileM * kBlock];
+  uint8_t b[2][kTileN * kBlock];
+  float as[2][kScaleGroup][kTileM];
+};
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int ntiles = tiles_m * tiles_n;
+  // XCD-aware remap: ids wg = 8 * local + xcd; give XCD x a contiguous range of tiles.
+  int tile = wg;
+  if (ntiles % 8 == 0) tile = (wg % 8) * (ntiles / 8) + wg / 8;
+  // grouped raster: groups of kGroupM M tiles walk across N
+  constexpr int kGroupM = 4;
+  const int group = tile / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int idx = tile - group * kGroupM * tiles_n;
+  tm = first_m + idx % gm;
+  tn = idx / gm;
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
+    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
+    int tiles_m, int tiles_n) {
+  __shared__ TileSmem sm;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
+  const int nkb = (int)(k / kBlock);
+  const float *bs_row = b_s + (n0 / kBlock) * nkb;
+
+  // staging assignment: chunk q = t + 512 i -> row q / 8, 16-byte chunk q % 8
+  const int st_c = t & 7, st_r = t >> 3;            // rows st_r + 64 i
+  const uint8_t *a_src[4];
+  bool a_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + st_r + 64 * i;
+    a_ok[i] = row < m;
+    a_src[i] = a + (a_ok[i] ? row : 0) * k + st_c * 16;
+  }
+  const uint8_t *b_src[2];
+  bool b_ok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = n0 + st_r + 64 * i;
+    b_ok[i] = row < n;
+    b_src[i] = b + (b_ok[i] ? row : 0) * k + st_c * 16;
+  }
+  // activation-scale staging: thread t -> row t / 2, four K blocks (t % 2) * 4 + 0..3
+  const int as_row = t >> 1, as_q = (t & 1) * 4;
+  const bool as_ok = m0 + as_row < m;
+  const float *as_src = a_s + (as_ok ? m0 + as_row : 0) * nkb;
+
+  uint4 ra[4], rb[2];
+  float ras[4];
+  auto load_stage = [&](int kb) {
+    const int64_t off = (int64_t)kb * kBlock;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ra[i] = a_ok[i] ? *(const uint4 *)(a_src[i] + off) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      rb[i] = b_ok[i] ? *(const uint4 *)(b_src[i] + off) : make_uint4(0, 0, 0, 0);
+  };
+  auto store_stage = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = st_r + 64 * i;
+      *(uint4 *)(&sm.a[s][r * kBlock + ((st_c ^ swz(r)) << 4)]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = st_r + 64 * i;
+      *(uint4 *)(&sm.b[s][r * kBlock + ((st_c ^ swz(r)) << 4)]) = rb[i];
+    }
+  };
+  auto load_scales = [&](int group) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kb = group * kScaleGroup + as_q + e;
+      ras[e] = (as_ok && kb < nkb) ? as_src[kb] : 0.0f;
+    }
+  };
+  auto store_scales = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.as[buf][as_q + e][as_row] = ras[e];
+  };
+
+  // wave tile origin inside the workgroup tile
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int fr = lane & 15, fq = lane >> 4;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_stage(0);
+  load_scales(0);
+  store_stage(0);
+  store_scales(0);
+  __syncthreads();
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const bool more = kb + 1 < nkb;
+    if (more) load_stage(kb + 1);
+    const int group = kb / kScaleGroup, kq = kb % kScaleGroup;
+    const bool next_group = (kq == 0) && ((group + 1) * kScaleGroup < nkb);
+    if (next_group) load_scales(group + 1);
+
+    const float sb = bs_row[kb];
+    float sc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = *(const float4 *)(&sm.as[group & 1][kq][wm + 16 * i + 4 * fq]);
+      sc[i][0] = v.x * sb;
+      sc[i][1] = v.y * sb;
+      sc[i][2] = v.z * sb;
+      sc[i][3] = v.w * sb;
+    }
+    i32x8 af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm + 16 * i + fr;
+      const uint8_t *base = &sm.a[cur][r * kBlock];
+      const uint4 lo = *(const uint4 *)(base + (((2 * fq) ^ swz(r)) << 4));
+      const uint4 hi = *(const uint4 *)(base + (((2 * fq + 1) ^ swz(r)) << 4));
+      af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn + 16 * j + fr;
+      const uint8_t *base = &sm.b[cur][r * kBlock];
+      const uint4 lo = *(const uint4 *)(base + (((2 * fq) ^ swz(r)) << 4));
+      const uint4 hi = *(const uint4 *)(base + (((2 * fq + 1) ^ swz(r)) << 4));
+      const i32x8 bfr = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 p = mfma_e4m3_16x16x128(af[i], bfr, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[e], sc[i][e], acc[i][j][e]);
+      }
+    }
+    if (more) store_stage(cur ^ 1);
+    if (kq == kScaleGroup - 1 && (group + 1) * kScaleGroup < nkb) store_scales((group + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn + 16 * j + fr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm + 16 * i + 4 * fq + e;
+        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][e]);
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream) {
+  if (m > 64) {
+    const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
+    if (c_bf16)
+      hipLaunchKernelGGL(block_gemm_tile_kernel<true>, grid, block, 0, stream, a, a_s, b, b_s, c, m,
+                         n, k, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL(block_gemm_tile_kernel<false>, grid, block, 0, stream, a, a_s, b, b_s, c,
+                         m, n, k, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), block(256);
   if (c_bf16)
     hipLaunchKernelGGL(block_gemm_simple_kernel<true>, grid, block, 0, stream, a, a_s, b, b_s, c,
