@@ -111,31 +111,62 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 //
 // Workgroup tile 256 (M) x 128 (N), 512 threads = 8 waves arranged 4 x 2, each
 // wave a 64 x 64 output tile (4 x 4 MFMA tiles).  Per 128-wide K block the
-// workgroup stages A[256 x 128] and B[128 x 128] (48 KiB of E4M3 codes) in LDS,
-// double-buffered: the global loads for block kb+1 are issued into registers
-// before block kb is computed and written to the other LDS buffer after it, so
-// one barrier per K block suffices.  A 128-column N tile lies inside one
-// 128-row weight block, so b_s is one scalar per K block.  Activation scales
-// are staged eight K blocks at a time, transposed to [kb][row] so a lane reads
-// the four rows it owns in one 16-byte LDS read.
+// workgroup needs A[256 x 128] and B[128 x 128] (48 KiB of E4M3 codes) plus the
+// 256 activation scales of that K block.  They arrive in LDS by direct
+// global->LDS loads (global_load_lds_dwordx4 / _dword), which need no staging
+// registers, into a three-stage ring: while K block kb is computed, blocks kb+1
+// and kb+2 are in flight, so each load has two K blocks of compute to land.
+// The loads are issued from inline assembly with explicit vmcnt waits: the
+// compiler's own handling of LDS DMA waits for every outstanding transfer
+// before any LDS read, which would serialize the ring.  Each wave issues the
+// same seven transfers per stage, so "vmcnt <= 7" means its part of stage kb
+// has landed; the barrier after the wait makes that true for all waves.
+//
+// A 128-column N tile lies inside one 128-row weight block, so b_s is one
+// scalar per K block.
 //
 // LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r is stored at
-// chunk c ^ swz(r), which spreads the 16 rows a fragment read touches over all
-// banks.
+// chunk slot c ^ swz(r), which spreads the 16 rows a fragment read touches
+// over all banks.  A DMA instruction writes 64 consecutive 16-byte slots (8
+// rows), so lane p fetches the global chunk that belongs in slot p.
 //
 // Tile order is XCD-aware: workgroup ids are dealt round-robin to the eight
 // XCDs, so consecutive tiles of the grouped raster order (4 M tiles by the N
 // tiles) are given to ids of the same XCD and share its L2.
 // ---------------------------------------------------------------------------
-constexpr int kTileM = 256, kTileN = 128, kThreads = 512, kScaleGroup = 8;
+constexpr int kTileM = 256, kTileN = 128, kThreads = 512, kStages = 3;
+constexpr int kDmaPerStage = 7;   // per wave: 4 (A) + 2 (B) + 1 (scales)
 
-struct TileSmem {
-  uint8_t a[2][kTileM * kBlock];
-  uint8_t b[2][kTileN * kBlock];
-  float as[2][kScaleGroup][kTileM];
+struct RingSmem {
+  uint8_t a[kStages][kTileM * kBlock];
+  uint8_t b[kStages][kTileN * kBlock];
+  float as[kStages][kTileM];
 };
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void *)p);
+}
+
+// 64 lanes x 16 bytes from per-lane global addresses to LDS [lds, lds + 1024).
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// active lanes x 4 bytes from per-lane global addresses to LDS [lds + 4 * lane].
+__device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_dma_all_but_one_stage() {
+  asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  static_assert(kDmaPerStage == 7, "the vmcnt immediate above must equal kDmaPerStage");
+}
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int &tm, int &tn) {
   const int ntiles = tiles_m * tiles_n;
@@ -157,73 +188,47 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     int tiles_m, int tiles_n) {
-  __shared__ TileSmem sm;
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  __shared__ __attribute__((aligned(1024))) RingSmem sm;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
   const int nkb = (int)(k / kBlock);
   const float *bs_row = b_s + (n0 / kBlock) * nkb;
 
-  // staging assignment: chunk q = t + 512 i -> row q / 8, 16-byte chunk q % 8
-  const int st_c = t & 7, st_r = t >> 3;            // rows st_r + 64 i
+  // DMA plan.  A: 8-row groups g = wave + 8 i (i < 4); B: g = wave + 8 i (i < 2).
+  // Lane p of a group fills slot p: row 8 g + p / 8, chunk slot p % 8.  Rows
+  // past the matrix edge re-read the last row (their outputs are never stored).
+  const int dr = lane >> 3, ds = lane & 7;
   const uint8_t *a_src[4];
-  bool a_ok[4];
+  const uint8_t *b_src[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = m0 + st_r + 64 * i;
-    a_ok[i] = row < m;
-    a_src[i] = a + (a_ok[i] ? row : 0) * k + st_c * 16;
+    const int row = 8 * (wave + 8 * i) + dr;
+    const int64_t grow = min(m0 + row, m - 1);
+    a_src[i] = a + grow * k + ((ds ^ swz(row)) << 4);
   }
-  const uint8_t *b_src[2];
-  bool b_ok[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int64_t row = n0 + st_r + 64 * i;
-    b_ok[i] = row < n;
-    b_src[i] = b + (b_ok[i] ? row : 0) * k + st_c * 16;
+    const int row = 8 * (wave + 8 * i) + dr;
+    const int64_t grow = min(n0 + row, n - 1);
+    b_src[i] = b + grow * k + ((ds ^ swz(row)) << 4);
   }
-  // activation-scale staging: thread t -> row t / 2, four K blocks (t % 2) * 4 + 0..3
-  const int as_row = t >> 1, as_q = (t & 1) * 4;
-  const bool as_ok = m0 + as_row < m;
-  const float *as_src = a_s + (as_ok ? m0 + as_row : 0) * nkb;
+  // scales: wave w, lanes 0..31 -> rows 32 w + lane
+  const int64_t srow = min(m0 + 32 * wave + (lane & 31), m - 1);
+  const float *as_src = a_s + srow * nkb;
 
-  uint4 ra[4], rb[2];
-  float ras[4];
-  auto load_stage = [&](int kb) {
+  auto issue = [&](int kb, int s) {
     const int64_t off = (int64_t)kb * kBlock;
+    const uint32_t abase = lds_addr(&sm.a[s][0]), bbase = lds_addr(&sm.b[s][0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = a_ok[i] ? *(const uint4 *)(a_src[i] + off) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) lds_dma16(a_src[i] + off, abase + (wave + 8 * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      rb[i] = b_ok[i] ? *(const uint4 *)(b_src[i] + off) : make_uint4(0, 0, 0, 0);
-  };
-  auto store_stage = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = st_r + 64 * i;
-      *(uint4 *)(&sm.a[s][r * kBlock + ((st_c ^ swz(r)) << 4)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = st_r + 64 * i;
-      *(uint4 *)(&sm.b[s][r * kBlock + ((st_c ^ swz(r)) << 4)]) = rb[i];
-    }
-  };
-  auto load_scales = [&](int group) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kb = group * kScaleGroup + as_q + e;
-      ras[e] = (as_ok && kb < nkb) ? as_src[kb] : 0.0f;
-    }
-  };
-  auto store_scales = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.as[buf][as_q + e][as_row] = ras[e];
+    for (int i = 0; i < 2; ++i) lds_dma16(b_src[i] + off, bbase + (wave + 8 * i) * 1024);
+    if (lane < 32) lds_dma4(as_src + kb, lds_addr(&sm.as[s][32 * wave]));
   };
 
-  // wave tile origin inside the workgroup tile
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int fr = lane & 15, fq = lane >> 4;
 
@@ -233,45 +238,41 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0);
-  load_scales(0);
-  store_stage(0);
-  store_scales(0);
-  __syncthreads();
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
 
+  int cur = 0;
   for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) load_stage(kb + 1);
-    const int group = kb / kScaleGroup, kq = kb % kScaleGroup;
-    const bool next_group = (kq == 0) && ((group + 1) * kScaleGroup < nkb);
-    if (next_group) load_scales(group + 1);
+    if (kb + 1 < nkb)
+      wait_dma_all_but_one_stage();
+    else
+      wait_dma_all();
+    workgroup_barrier();
+    if (kb + 2 < nkb) issue(kb + 2, cur == 0 ? 2 : cur - 1);
 
     const float sb = bs_row[kb];
     float sc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 v = *(const float4 *)(&sm.as[group & 1][kq][wm + 16 * i + 4 * fq]);
-      sc[i][0] = v.x * sb;
-      sc[i][1] = v.y * sb;
-      sc[i][2] = v.z * sb;
-      sc[i][3] = v.w * sb;
+      const f32x4 v = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[i][e] = v[e] * sb;
     }
     i32x8 af[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm + 16 * i + fr;
-      const uint8_t *base = &sm.a[cur][r * kBlock];
-      const uint4 lo = *(const uint4 *)(base + (((2 * fq) ^ swz(r)) << 4));
-      const uint4 hi = *(const uint4 *)(base + (((2 * fq + 1) ^ swz(r)) << 4));
+      const uint4 *base = (const uint4 *)&sm.a[cur][r * kBlock];
+      const uint4 lo = base[(2 * fq) ^ swz(r)];
+      const uint4 hi = base[(2 * fq + 1) ^ swz(r)];
       af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn + 16 * j + fr;
-      const uint8_t *base = &sm.b[cur][r * kBlock];
-      const uint4 lo = *(const uint4 *)(base + (((2 * fq) ^ swz(r)) << 4));
-      const uint4 hi = *(const uint4 *)(base + (((2 * fq + 1) ^ swz(r)) << 4));
+      const uint4 *base = (const uint4 *)&sm.b[cur][r * kBlock];
+      const uint4 lo = base[(2 * fq) ^ swz(r)];
+      const uint4 hi = base[(2 * fq + 1) ^ swz(r)];
       const i32x8 bfr = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -280,9 +281,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[e], sc[i][e], acc[i][j][e]);
       }
     }
-    if (more) store_stage(cur ^ 1);
-    if (kq == kScaleGroup - 1 && (group + 1) * kScaleGroup < nkb) store_scales((group + 1) & 1);
-    __syncthreads();
+    cur = cur == kStages - 1 ? 0 : cur + 1;
   }
 
 #pragma unroll
