@@ -109,38 +109,43 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 // ---------------------------------------------------------------------------
 // Tiled kernel for large M.
 //
-// Workgroup tile 256 (M) x 128 (N), 512 threads = 8 waves arranged 4 x 2, each
-// wave a 64 x 64 output tile (4 x 4 MFMA tiles).  Per 128-wide K block the
-// workgroup needs A[256 x 128] and B[128 x 128] (48 KiB of E4M3 codes) plus the
-// 256 activation scales of that K block.  They arrive in LDS by direct
-// global->LDS loads (global_load_lds_dwordx4 / _dword), which need no staging
-// registers, into a three-stage ring: while K block kb is computed, blocks kb+1
-// and kb+2 are in flight, so each load has two K blocks of compute to land.
-// The loads are issued from inline assembly with explicit vmcnt waits: the
-// compiler's own handling of LDS DMA waits for every outstanding transfer
-// before any LDS read, which would serialize the ring.  Each wave issues the
-// same seven transfers per stage, so "vmcnt <= 7" means its part of stage kb
-// has landed; the barrier after the wait makes that true for all waves.
+// Workgroup tile 256 (M) x 256 (N), 512 threads = 8 waves arranged 4 x 2; each
+// wave owns a 64 x 128 output tile (4 x 8 MFMA tiles, 128 FP32 accumulators
+// per lane).  The tile size is set by the operand feed: every K block brings
+// (256 + 256) x 128 bytes of E4M3 codes from L2 into LDS, and on this part the
+// L2 -> LDS path, not the matrix cores, is what runs out first, so the widest
+// tile whose accumulators still fit in registers moves the fewest bytes per
+// MFMA.
 //
-// A 128-column N tile lies inside one 128-row weight block, so b_s is one
-// scalar per K block.
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4, and
+// _dword for the 256 activation scales of the K block) into a two-stage ring:
+// K block kb+1 is loaded while kb is computed.  The loads are issued from
+// inline assembly with an explicit vmcnt wait, because the compiler's own
+// handling of LDS DMA waits for every outstanding transfer before any LDS
+// read.  Global addresses are a per-lane 32-bit offset on a wave-uniform
+// 64-bit base, so advancing to the next K block costs scalar adds only.
+//
+// Each wave's 128 columns lie inside one 128-row weight block, so b_s is one
+// scalar per wave and K block.  The per-K-block rescale (4 FMAs per MFMA) is
+// software-pipelined by hand two MFMAs behind the MFMA that produced its
+// partial, which keeps only three partials live; the scheduler would otherwise
+// hoist all 32 MFMAs of a K block and run out of registers.
 //
 // LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r is stored at
-// chunk slot c ^ swz(r), which spreads the 16 rows a fragment read touches
-// over all banks.  A DMA instruction writes 64 consecutive 16-byte slots (8
-// rows), so lane p fetches the global chunk that belongs in slot p.
+// slot c ^ swz(r), so the 16 rows a fragment read touches hit distinct banks.
+// A DMA instruction fills 64 consecutive 16-byte slots (8 rows): lane p
+// fetches the global chunk that belongs in slot p.
 //
 // Tile order is XCD-aware: workgroup ids are dealt round-robin to the eight
 // XCDs, so consecutive tiles of the grouped raster order (4 M tiles by the N
-// tiles) are given to ids of the same XCD and share its L2.
+// tiles) go to ids of the same XCD and share its L2.
 // ---------------------------------------------------------------------------
-constexpr int kTileM = 256, kTileN = 128, kThreads = 512, kStages = 3;
-constexpr int kDmaPerStage = 7;   // per wave: 4 (A) + 2 (B) + 1 (scales)
+constexpr int kTileM = 256, kTileN = 256, kThreads = 512;
 
-struct RingSmem {
-  uint8_t a[kStages][kTileM * kBlock];
-  uint8_t b[kStages][kTileN * kBlock];
-  float as[kStages][kTileM];
+struct TileSmem {
+  uint8_t a[2][kTileM * kBlock];
+  uint8_t b[2][kTileN * kBlock];
+  float as[2][kTileM];
 };
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -149,22 +154,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void *)p);
 }
 
-// 64 lanes x 16 bytes from per-lane global addresses to LDS [lds, lds + 1024).
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+// 64 lanes x 16 bytes from base + voff (per lane) into LDS [lds, lds + 1024).
+__device__ __forceinline__ void lds_dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 
-// active lanes x 4 bytes from per-lane global addresses to LDS [lds + 4 * lane].
-__device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+// active lanes x 4 bytes from base + voff into LDS [lds + 4 * lane].
+__device__ __forceinline__ void lds_dma4(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 
-__device__ __forceinline__ void wait_dma_all_but_one_stage() {
-  asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-  static_assert(kDmaPerStage == 7, "the vmcnt immediate above must equal kDmaPerStage");
-}
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -183,111 +184,122 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
   tn = idx / gm;
 }
 
+__device__ __forceinline__ i32x8 frag_from_lds(const uint8_t *row_base, int fq, int r) {
+  const uint4 *base = (const uint4 *)row_base;
+  const uint4 lo = base[(2 * fq) ^ swz(r)];
+  const uint4 hi = base[(2 * fq + 1) ^ swz(r)];
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
 template <bool kBf16Out>
 __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) RingSmem sm;
+  __shared__ __attribute__((aligned(1024))) TileSmem sm;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
   const int nkb = (int)(k / kBlock);
-  const float *bs_row = b_s + (n0 / kBlock) * nkb;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
+  const int64_t grid_n = (n + kBlock - 1) / kBlock;
+  const float *bs_row = b_s + min((n0 + wn) / kBlock, grid_n - 1) * nkb;
 
-  // DMA plan.  A: 8-row groups g = wave + 8 i (i < 4); B: g = wave + 8 i (i < 2).
-  // Lane p of a group fills slot p: row 8 g + p / 8, chunk slot p % 8.  Rows
-  // past the matrix edge re-read the last row (their outputs are never stored).
+  // DMA plan: 8-row groups g = wave + 8 i (i < 4) of A and of B; lane p of a
+  // group fills slot p (row 8 g + p / 8, chunk slot p % 8).  Rows past the
+  // matrix edge re-read the last row; their outputs are never stored.
   const int dr = lane >> 3, ds = lane & 7;
-  const uint8_t *a_src[4];
-  const uint8_t *b_src[2];
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 8 * (wave + 8 * i) + dr;
-    const int64_t grow = min(m0 + row, m - 1);
-    a_src[i] = a + grow * k + ((ds ^ swz(row)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 8 * (wave + 8 * i) + dr;
-    const int64_t grow = min(n0 + row, n - 1);
-    b_src[i] = b + grow * k + ((ds ^ swz(row)) << 4);
+    a_off[i] = (uint32_t)(min(m0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
+    b_off[i] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
   }
   // scales: wave w, lanes 0..31 -> rows 32 w + lane
-  const int64_t srow = min(m0 + 32 * wave + (lane & 31), m - 1);
-  const float *as_src = a_s + srow * nkb;
+  const uint32_t s_off = (uint32_t)(min(m0 + 32 * wave + (lane & 31), m - 1) * nkb * 4);
+  const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]),
+                 lds_s = lds_addr(&sm.as[0][0]);
 
   auto issue = [&](int kb, int s) {
-    const int64_t off = (int64_t)kb * kBlock;
-    const uint32_t abase = lds_addr(&sm.a[s][0]), bbase = lds_addr(&sm.b[s][0]);
+    const uint8_t *ab = a + (int64_t)kb * kBlock;
+    const uint8_t *bb = b + (int64_t)kb * kBlock;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(a_src[i] + off, abase + (wave + 8 * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(b_src[i] + off, bbase + (wave + 8 * i) * 1024);
-    if (lane < 32) lds_dma4(as_src + kb, lds_addr(&sm.as[s][32 * wave]));
+    for (int i = 0; i < 4; ++i) {
+      lds_dma16(ab, a_off[i], lds_a + s * (kTileM * kBlock) + (wave + 8 * i) * 1024);
+      lds_dma16(bb, b_off[i], lds_b + s * (kTileN * kBlock) + (wave + 8 * i) * 1024);
+    }
+    if (lane < 32) lds_dma4(a_s + kb, s_off, lds_s + s * (kTileM * 4) + 32 * wave * 4);
   };
 
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int fr = lane & 15, fq = lane >> 4;
-
-  f32x4 acc[4][4];
+  f32x4 acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  if (nkb > 1) issue(1, 1);
-
-  int cur = 0;
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb)
-      wait_dma_all_but_one_stage();
-    else
-      wait_dma_all();
-    workgroup_barrier();
-    if (kb + 2 < nkb) issue(kb + 2, cur == 0 ? 2 : cur - 1);
-
-    const float sb = bs_row[kb];
+  auto step = [&](int kb, int cur) {
+    wait_dma_all();
+    workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
+    if (kb + 1 < nkb) issue(kb + 1, cur ^ 1);
+    const float sbv = bs_row[kb];
     float sc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 v = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sc[i][e] = v[e] * sb;
+      for (int e = 0; e < 4; ++e) sc[i][e] = v[e] * sbv;
     }
     i32x8 af[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm + 16 * i + fr;
-      const uint4 *base = (const uint4 *)&sm.a[cur][r * kBlock];
-      const uint4 lo = base[(2 * fq) ^ swz(r)];
-      const uint4 hi = base[(2 * fq + 1) ^ swz(r)];
-      af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      af[i] = frag_from_lds(&sm.a[cur][r * kBlock], fq, r);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    auto read_b = [&](int j) {
       const int r = wn + 16 * j + fr;
-      const uint4 *base = (const uint4 *)&sm.b[cur][r * kBlock];
-      const uint4 lo = base[(2 * fq) ^ swz(r)];
-      const uint4 hi = base[(2 * fq + 1) ^ swz(r)];
-      const i32x8 bfr = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      return frag_from_lds(&sm.b[cur][r * kBlock], fq, r);
+    };
+    // MFMA q = 4 j + i; its rescale runs two MFMAs later (ring of 3 partials).
+    i32x8 bcur = read_b(0), bnext;
+    f32x4 part[3];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j + 1 < 8) bnext = read_b(j + 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 p = mfma_e4m3_16x16x128(af[i], bfr, f32x4{0.f, 0.f, 0.f, 0.f});
+        const int q = 4 * j + i;
+        part[q % 3] = mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (q >= 2) {
+          const int qp = q - 2, ip = qp % 4, jp = qp / 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[e], sc[i][e], acc[i][j][e]);
+          for (int e = 0; e < 4; ++e)
+            acc[ip][jp][e] = __builtin_fmaf(part[qp % 3][e], sc[ip][e], acc[ip][jp][e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (j + 1 < 8) bcur = bnext;
     }
-    cur = cur == kStages - 1 ? 0 : cur + 1;
-  }
+#pragma unroll
+    for (int qp = 30; qp < 32; ++qp) {
+      const int ip = qp % 4, jp = qp / 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[ip][jp][e] = __builtin_fmaf(part[qp % 3][e], sc[ip][e], acc[ip][jp][e]);
+    }
+  };
+
+  issue(0, 0);
+#pragma nounroll
+  for (int kb = 0; kb < nkb; ++kb) step(kb, kb & 1);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const int64_t col = n0 + wn + 16 * j + fr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -302,7 +314,9 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream) {
-  if (m > 64) {
+  // the tiled kernel addresses A, B and a_s with 32-bit per-lane offsets
+  const bool offsets_fit = m * k < ((int64_t)1 << 32) && n * k < ((int64_t)1 << 32);
+  if (m > 64 && offsets_fit) {
     const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
     if (c_bf16)
