@@ -11,11 +11,13 @@
 // tensor form one contiguous sequence [nblocks, 128] and the scales one
 // contiguous [nblocks] vector.  The kernel works on that flat sequence.
 //
-// Work split: four lanes own one block, 32 elements each; a wave covers 16
-// blocks and a 256-thread workgroup 64.  Lane (4b + j) of a wave reads the
-// 16-byte chunks j, j+4, j+8, j+12 of its block, so each load instruction
-// fetches 64 contiguous bytes per block.  The block's amax is reduced over the
-// four lanes with two DPP quad permutations.
+// Work split (bf16 input): sixteen lanes own one block, 8 elements (16 bytes)
+// each, so every load instruction of a wave reads 1 KiB of four consecutive
+// blocks and every code store writes their 512 contiguous bytes: both cover
+// whole cache lines, which lets the loads stream past the caches.  A wave
+// covers 16 blocks in four such instructions; the block's amax is reduced over
+// its 16-lane row with four DPP row rotations.  (fp32 inputs, used only for
+// small activations, keep four lanes per block.)
 //
 // Exact quotient: the codes must equal E4M3(fl32(x / s)).  For bf16 inputs
 // the per-element division is replaced by r = fl32(1 / s) (one IEEE division
@@ -25,6 +27,10 @@
 // significand (checked exhaustively, 2^30 pairs, by tests/division_identity.c);
 // residuals are exact whenever |x| >= 2^-102, and below that |x / s| < 2^-80
 // encodes to zero either way.  The sign convention of e keeps x = -0 at -0.
+// The scale itself, fl32(amax / 448), is computed the same way from the
+// constant fl32(1/448); the same file checks that against the IEEE division
+// for every fp32 amax from fl32(1e-4) to the largest finite value.  Under
+// ue8m0 the scale is a power of two and its reciprocal is exact bit arithmetic.
 // fp32 inputs use the IEEE division directly.
 #include "device_common.h"
 #include "launch.h"
@@ -38,6 +44,39 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kFp8Max = 448.0f;
 constexpr float kAmaxFloor = 1e-4f;   // fl32(1e-4) = 0x38D1B717
+constexpr float kInv448 = 0x1.24924Ap-9f;   // fl32(1/448) = 0x3B124925
+
+// DPP row rotations (within each 16-lane row).
+constexpr int kDppRowRor8 = 0x128, kDppRowRor4 = 0x124, kDppRowRor2 = 0x122, kDppRowRor1 = 0x121;
+
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor8, 0xF, 0xF, false);
+  v = v > o ? v : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor4, 0xF, 0xF, false);
+  v = v > o ? v : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor2, 0xF, 0xF, false);
+  v = v > o ? v : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor1, 0xF, 0xF, false);
+  return v > o ? v : o;
+}
+
+// s = fl32(amax / 448) and r = fl32(1 / s), amax given as the bits of a
+// non-negative fp32 (bf16 path: reciprocal-and-residual form of the division).
+__device__ __forceinline__ void block_scale_fast(uint32_t amax_bits, bool ue8m0, float &s, float &r) {
+  float amax = __uint_as_float(amax_bits);
+  amax = amax > kAmaxFloor ? amax : kAmaxFloor;
+  const float q0 = amax * kInv448;
+  const float e = __builtin_fmaf(q0, kFp8Max, -amax);
+  s = __builtin_fmaf(-e, kInv448, q0);
+  if (ue8m0) {
+    // smallest power of two >= s; its reciprocal is the mirrored exponent
+    const uint32_t p = (__float_as_uint(s) + 0x007FFFFFu) & 0xFF800000u;
+    s = __uint_as_float(p);
+    r = __uint_as_float(0x7F000000u - p);
+  } else {
+    r = 1.0f / s;                                         // IEEE, correctly rounded
+  }
+}
 
 // s and r = fl32(1/s) from the block's amax (given as the bits of a
 // non-negative fp32).
@@ -65,7 +104,7 @@ __device__ __forceinline__ float quotient_f32(float x, float s) {
 }
 
 // 8 bf16 (one 16-byte chunk) -> 8 codes (two dwords).
-__device__ __forceinline__ uint2 encode_chunk_bf16(uint4 w, float s, float r) {
+__device__ __forceinline__ u32x2 encode_chunk_bf16(u32x4 w, float s, float r) {
   const uint32_t d[4] = {w.x, w.y, w.z, w.w};
   uint32_t out[2];
 #pragma unroll
@@ -77,55 +116,46 @@ __device__ __forceinline__ uint2 encode_chunk_bf16(uint4 w, float s, float r) {
     c = cvt_pk_e4m3<true>(quotient_bf16(x2, s, r), quotient_bf16(x3, s, r), c);
     out[h] = c;
   }
-  return make_uint2(out[0], out[1]);
+  return u32x2{out[0], out[1]};
 }
 
 template <bool kUe8m0>
-__global__ __launch_bounds__(256) void act_quant_bf16_kernel(const uint4 *__restrict__ x,
-                                                              uint2 *__restrict__ y,
+__global__ __launch_bounds__(256) void act_quant_bf16_kernel(const u32x4 *__restrict__ x,
+                                                              u32x2 *__restrict__ y,
                                                               float *__restrict__ scales,
                                                               int64_t nblocks) {
   const int lane = threadIdx.x & 63;
-  const int64_t blk = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + (lane >> 2);
-  const int sub = lane & 3;
-  const bool valid = blk < nblocks;
+  const int row = lane >> 4, sub = lane & 15;
+  const int64_t blk0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + row;
 
-  uint4 v[4];
-  if (valid) {
-    const uint4 *xb = x + blk * 16;          // 16 chunks of 8 bf16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = xb[4 * i + sub];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
-  }
-
-  // |x| max on the packed bf16 halves: clearing the sign bits leaves
-  // magnitudes whose integer order is their numeric order.
-  u16x2 m2 = {0, 0};
+  u32x4 v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int64_t blk = blk0 + 4 * i;                 // 16 chunks of 8 bf16 per block
+    v[i] = blk < nblocks ? load_stream(x + blk * 16 + sub) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t blk = blk0 + 4 * i;
+    // |x| max on the packed bf16 halves: clearing the sign bits leaves
+    // magnitudes whose integer order is their numeric order.
+    u16x2 m2 = {0, 0};
     const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
-  }
-  uint32_t amax = (uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16;
-  amax = quad_max_u32(amax);
-
-  float s, r;
-  block_scale(amax, kUe8m0, s, r);
-
-  if (valid) {
-    uint2 *yb = y + blk * 16;                // 16 groups of 8 codes
-#pragma unroll
-    for (int i = 0; i < 4; ++i) yb[4 * i + sub] = encode_chunk_bf16(v[i], s, r);
-    if (sub == 0) scales[blk] = s;
+    const uint32_t amax = row_max_u32((uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16);
+    float s, r;
+    block_scale_fast(amax, kUe8m0, s, r);
+    if (blk < nblocks) {
+      y[blk * 16 + sub] = encode_chunk_bf16(v[i], s, r);
+      if (sub == 0) scales[blk] = s;
+    }
   }
 }
 
 template <bool kUe8m0>
-__global__ __launch_bounds__(256) void act_quant_f32_kernel(const uint4 *__restrict__ x,
+__global__ __launch_bounds__(256) void act_quant_f32_kernel(const u32x4 *__restrict__ x,
                                                              uint32_t *__restrict__ y,
                                                              float *__restrict__ scales,
                                                              int64_t nblocks) {
@@ -134,14 +164,14 @@ __global__ __launch_bounds__(256) void act_quant_f32_kernel(const uint4 *__restr
   const int sub = lane & 3;
   const bool valid = blk < nblocks;
 
-  uint4 v[8];
+  u32x4 v[8];
   if (valid) {
-    const uint4 *xb = x + blk * 32;          // 32 chunks of 4 fp32
+    const u32x4 *xb = x + blk * 32;          // 32 chunks of 4 fp32
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = xb[4 * i + sub];
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) v[i] = u32x4{0, 0, 0, 0};
   }
 
   uint32_t amax = 0;
@@ -182,17 +212,17 @@ hipError_t launch_act_quant(const void *x, bool x_bf16, int64_t nblocks, bool ue
   if (x_bf16) {
     if (ue8m0)
       hipLaunchKernelGGL(act_quant_bf16_kernel<true>, grid, block, 0, stream,
-                         (const uint4 *)x, (uint2 *)y, s, nblocks);
+                         (const u32x4 *)x, (u32x2 *)y, s, nblocks);
     else
       hipLaunchKernelGGL(act_quant_bf16_kernel<false>, grid, block, 0, stream,
-                         (const uint4 *)x, (uint2 *)y, s, nblocks);
+                         (const u32x4 *)x, (u32x2 *)y, s, nblocks);
   } else {
     if (ue8m0)
       hipLaunchKernelGGL(act_quant_f32_kernel<true>, grid, block, 0, stream,
-                         (const uint4 *)x, (uint32_t *)y, s, nblocks);
+                         (const u32x4 *)x, (uint32_t *)y, s, nblocks);
     else
       hipLaunchKernelGGL(act_quant_f32_kernel<false>, grid, block, 0, stream,
-                         (const uint4 *)x, (uint32_t *)y, s, nblocks);
+                         (const u32x4 *)x, (uint32_t *)y, s, nblocks);
   }
   return hipGetLastError();
 }

@@ -12,6 +12,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 128;   // the only block size implemented
 
@@ -46,5 +48,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
   return __builtin_bit_cast(uint32_t, h);
 }
+
+// Streaming (nontemporal) loads for inputs read exactly once.  Only used where
+// each load instruction of a wave covers whole cache lines: a line read in
+// parts by several streaming instructions would be fetched more than once.
+__device__ __forceinline__ u32x4 load_stream(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x2 load_stream(const u32x2 *p) { return __builtin_nontemporal_load(p); }
 
 }  // namespace fp8bsq

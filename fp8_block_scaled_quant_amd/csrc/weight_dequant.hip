@@ -8,14 +8,16 @@
 // masked.
 //
 // The tile-per-workgroup structure is kept because it makes the scale a
-// workgroup-uniform value (one scalar load).  Inside the tile, 8 lanes cover
-// one 128-column row segment with 16-byte loads (16 codes each) and a
-// 256-thread workgroup covers 32 rows per pass; the four passes' loads are all
-// issued before any conversion so each lane has 64 bytes in flight.  Codes go
-// to FP32 with the hardware E4M3 conversion (exact), one FP32 multiply, then
-// the hardware round-to-nearest-even BF16 pack for BF16 output.
+// workgroup-uniform value (one scalar load).  Inside the tile, 16 lanes cover
+// one 128-column row segment, 8 codes each: every 8-byte load instruction then
+// reads whole 128-byte lines of codes (so the loads can stream past the
+// caches) and every 16-byte bf16 store writes whole lines.  A 256-thread
+// workgroup covers 16 rows per pass; all eight passes' loads are issued
+// before any conversion.  Codes go to FP32 with the hardware E4M3 conversion
+// (exact), one FP32 multiply, then the hardware round-to-nearest-even BF16
+// pack for BF16 output.
 //
-// Shapes with n % 16 != 0, or unaligned pointers, take an element-wise kernel.
+// Shapes with n % 8 != 0, or unaligned pointers, take an element-wise kernel.
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,41 +34,33 @@ __global__ __launch_bounds__(256) void dequant_tile_kernel(const uint8_t *__rest
   const int64_t tile_c = blockIdx.x, tile_r = blockIdx.y;
   const float sc = s[tile_r * grid_n + tile_c];
   const int tid = threadIdx.x;
-  const int64_t col = tile_c * kBlock + (tid & 7) * 16;
-  if (col >= n) return;                        // n % 16 == 0: chunks never straddle the edge
-  const int64_t row0 = tile_r * kBlock + (tid >> 3);
+  const int64_t col = tile_c * kBlock + (tid & 15) * 8;
+  if (col >= n) return;                        // n % 8 == 0: chunks never straddle the edge
+  const int64_t row0 = tile_r * kBlock + (tid >> 4);
 
-  uint4 v[4];
+  u32x2 v[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int64_t row = row0 + 32 * p;
-    v[p] = row < m ? *(const uint4 *)(x + row * n + col) : make_uint4(0, 0, 0, 0);
+  for (int p = 0; p < 8; ++p) {
+    const int64_t row = row0 + 16 * p;
+    v[p] = row < m ? load_stream((const u32x2 *)(x + row * n + col)) : u32x2{0, 0};
   }
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int64_t row = row0 + 32 * p;
+  for (int p = 0; p < 8; ++p) {
+    const int64_t row = row0 + 16 * p;
     if (row >= m) break;
-    const uint32_t d[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-    float f[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 q = e4m3x4_to_f32(d[j]);
-      f[4 * j + 0] = q.x * sc;
-      f[4 * j + 1] = q.y * sc;
-      f[4 * j + 2] = q.z * sc;
-      f[4 * j + 3] = q.w * sc;
-    }
+    const f32x4 lo = e4m3x4_to_f32(v[p].x), hi = e4m3x4_to_f32(v[p].y);
+    const float f[8] = {lo.x * sc, lo.y * sc, lo.z * sc, lo.w * sc,
+                        hi.x * sc, hi.y * sc, hi.z * sc, hi.w * sc};
     if (kBf16Out) {
-      uint4 *dst = (uint4 *)((uint16_t *)y + row * n + col);
-      dst[0] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-      dst[1] = make_uint4(pack_bf16x2(f[8], f[9]), pack_bf16x2(f[10], f[11]),
-                          pack_bf16x2(f[12], f[13]), pack_bf16x2(f[14], f[15]));
+      u32x4 *dst = (u32x4 *)((uint16_t *)y + row * n + col);
+      *dst = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7])};
     } else {
-      float4 *dst = (float4 *)((float *)y + row * n + col);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dst[j] = make_float4(f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]);
+      u32x4 *dst = (u32x4 *)((float *)y + row * n + col);
+      dst[0] = u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                     __float_as_uint(f[3])};
+      dst[1] = u32x4{__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                     __float_as_uint(f[7])};
     }
   }
 }
@@ -95,7 +89,7 @@ __global__ __launch_bounds__(256) void dequant_elementwise_kernel(const uint8_t 
 hipError_t launch_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, void *y,
                                  bool y_bf16, hipStream_t stream) {
   const int64_t grid_n = (n + kBlock - 1) / kBlock, grid_m = (m + kBlock - 1) / kBlock;
-  const bool vec = (n % 16 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0) &&
+  const bool vec = (n % 8 == 0) && ((uintptr_t)x % 8 == 0) && ((uintptr_t)y % 16 == 0) &&
                    grid_m <= 65535;
   if (vec) {
     const dim3 grid((unsigned)grid_n, (unsigned)grid_m), block(256);

@@ -92,7 +92,7 @@ FP8BSQ_API int fp8_act_quant(const void *x, int x_dtype, int64_t rows, int64_t k
  *            FP8BSQ_BF16 gives that product rounded to nearest even bf16.
  *
  * Results are bit-identical to the CPU oracle for finite scales.  Inputs with
- * n % 16 == 0 and 16-byte-aligned x and y take the vectorized path.
+ * n % 8 == 0, 8-byte-aligned x and 16-byte-aligned y take the vectorized path.
  */
 FP8BSQ_API int fp8_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, int block_size,
                        void *y, int y_dtype, void *hip_stream);
