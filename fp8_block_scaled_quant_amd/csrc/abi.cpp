@@ -29,7 +29,7 @@ int fp8_act_quant(const void *x, int x_dtype, int64_t rows, int64_t k, int block
   if (!aligned(x, 16) || !aligned(y, 8) || !aligned(s, 4)) return FP8BSQ_EALIGN;
   if (rows >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
   const int64_t nblocks = rows * (k / block_size);
-  if ((nblocks + 63) / 64 >= kMaxDim) return FP8BSQ_ERANGE;
+  if ((nblocks + 31) / 32 >= kMaxDim) return FP8BSQ_ERANGE;
   return launch_status(fp8bsq::launch_act_quant(x, x_dtype == FP8BSQ_BF16, nblocks,
                                                 scale_fmt == FP8BSQ_SCALE_UE8M0, y, s,
                                                 (hipStream_t)hip_stream));

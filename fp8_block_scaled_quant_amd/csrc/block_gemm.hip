@@ -309,6 +309,92 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny kernel for M <= 64 (decode).  The weight B [n, k] is streamed from
+// HBM exactly once and dominates the traffic, so the kernel is built to keep
+// many weight bytes in flight: each wave owns 16 weight rows over the whole
+// K range and keeps the B fragments of the next kDepth K blocks in registers,
+// issuing the load for block kb + kDepth as it consumes block kb.  A (at most
+// 64 x k codes) is read through the caches by every wave; the activation
+// scales are staged once per workgroup in LDS, transposed to [kb][row].  The
+// 16 weight rows of a wave lie in one 128-row weight block, so b_s is one
+// scalar per K block.  kMT = ceil(m / 16) MFMA tiles cover the activation rows.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeWaves = 4, kDepth = 8, kDecodeMaxM = 64, kDecodeMaxKb = 160;
+
+template <bool kBf16Out, int kMT>
+__global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
+    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k) {
+  __shared__ float as_t[kDecodeMaxKb][kDecodeMaxM];   // [kb][row], zero-padded rows
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nkb = (int)(k / kBlock);
+  for (int i = t; i < nkb * kDecodeMaxM; i += 64 * kDecodeWaves) {
+    const int kb = i / kDecodeMaxM, r = i % kDecodeMaxM;
+    as_t[kb][r] = r < m ? a_s[(int64_t)r * nkb + kb] : 0.0f;
+  }
+  __syncthreads();
+
+  const int64_t n0 = ((int64_t)blockIdx.x * kDecodeWaves + wave) * 16;
+  if (n0 >= n) return;                                  // whole wave past the edge
+  const int fr = lane & 15, fq = lane >> 4;
+  const float *bs_row = b_s + (n0 / kBlock) * nkb;
+  // lane -> (row fr, bytes [16 fq, 16 fq + 16) and [64 + 16 fq, ...)) of a K block;
+  // A and B use the same byte -> k assignment.
+  const uint8_t *b_src = b + min(n0 + fr, n - 1) * k + 16 * fq;
+  const uint8_t *a_src[kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) a_src[mt] = a + min((int64_t)(16 * mt + fr), m - 1) * k + 16 * fq;
+
+  auto load_b = [&](int kb) {
+    const uint8_t *p = b_src + (int64_t)kb * kBlock;
+    const uint4 lo = *(const uint4 *)p, hi = *(const uint4 *)(p + 64);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto load_a = [&](int mt, int kb) {
+    const uint8_t *p = a_src[mt] + (int64_t)kb * kBlock;
+    const uint4 lo = *(const uint4 *)p, hi = *(const uint4 *)(p + 64);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  f32x4 acc[kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  i32x8 bq[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (d < nkb) bq[d] = load_b(d);
+
+  for (int kb0 = 0; kb0 < nkb; kb0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int kb = kb0 + d;
+      if (kb < nkb) {
+        const i32x8 bf = bq[d];
+        if (kb + kDepth < nkb) bq[d] = load_b(kb + kDepth);
+        const float sb = bs_row[kb];
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          const f32x4 sa = *(const f32x4 *)&as_t[kb][16 * mt + 4 * fq];
+          const f32x4 p = mfma_e4m3_16x16x128(load_a(mt, kb), bf, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(p[e], sa[e] * sb, acc[mt][e]);
+        }
+      }
+    }
+  }
+
+  const int64_t col = n0 + fr;
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = 16 * mt + 4 * fq + e;
+      if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][e]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
@@ -325,6 +411,27 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
     else
       hipLaunchKernelGGL(block_gemm_tile_kernel<false>, grid, block, 0, stream, a, a_s, b, b_s, c,
                          m, n, k, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
+  if (m <= kDecodeMaxM && k / kBlock <= kDecodeMaxKb) {
+    const dim3 grid((unsigned)((n + 16 * kDecodeWaves - 1) / (16 * kDecodeWaves))),
+        block(64 * kDecodeWaves);
+#define FP8BSQ_DECODE(MT)                                                                        \
+  do {                                                                                           \
+    if (c_bf16)                                                                                  \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT>), grid, block, 0, stream, a, a_s, b, \
+                         b_s, c, m, n, k);                                                       \
+    else                                                                                         \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT>), grid, block, 0, stream, a, a_s,  \
+                         b, b_s, c, m, n, k);                                                    \
+  } while (0)
+    switch ((m + 15) / 16) {
+      case 1: FP8BSQ_DECODE(1); break;
+      case 2: FP8BSQ_DECODE(2); break;
+      case 3: FP8BSQ_DECODE(3); break;
+      default: FP8BSQ_DECODE(4); break;
+    }
+#undef FP8BSQ_DECODE
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), block(256);
