@@ -312,87 +312,126 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 // ---------------------------------------------------------------------------
 // Skinny kernel for M <= 64 (decode).  The weight B [n, k] is streamed from
 // HBM exactly once and dominates the traffic, so the kernel is built to keep
-// many weight bytes in flight: each wave owns 16 weight rows over the whole
-// K range and keeps the B fragments of the next kDepth K blocks in registers,
-// issuing the load for block kb + kDepth as it consumes block kb.  A (at most
-// 64 x k codes) is read through the caches by every wave; the activation
-// scales are staged once per workgroup in LDS, transposed to [kb][row].  The
-// 16 weight rows of a wave lie in one 128-row weight block, so b_s is one
-// scalar per K block.  kMT = ceil(m / 16) MFMA tiles cover the activation rows.
+// many weight bytes in flight with many waves.  A workgroup owns 16 * kNT
+// weight rows; its four waves split the K range four ways (partial sums meet
+// in LDS at the end), and each wave keeps the B fragments of its next kDepth
+// K blocks in registers, issuing the load for block kb + kDepth as it consumes
+// block kb.  A (at most 64 x k codes) is read through the caches as it is
+// used: holding its fragments in the ring too was measured slower, because the
+// extra registers halve the waves per SIMD.  kNT = 2 for larger M halves the
+// activation re-reads.  The activation scales are staged once per
+// workgroup in LDS, transposed to [kb][row].  A wave's weight rows lie in one
+// 128-row weight block, so b_s is one scalar per K block.  kMT = ceil(m / 16)
+// MFMA tiles cover the activation rows.
 // ---------------------------------------------------------------------------
-constexpr int kDecodeWaves = 4, kDepth = 8, kDecodeMaxM = 64, kDecodeMaxKb = 160;
+constexpr int kDecodeWaves = 4, kDecodeMaxM = 64, kDecodeMaxKb = 160;
 
-template <bool kBf16Out, int kMT>
+template <bool kBf16Out, int kMT, int kNT, int kDepth>
 __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k) {
-  __shared__ float as_t[kDecodeMaxKb][kDecodeMaxM];   // [kb][row], zero-padded rows
+  constexpr int kRows = 16 * kMT;
+  __shared__ float as_t[kDecodeMaxKb][kRows];   // [kb][row], zero-padded rows
+  __shared__ f32x4 red[kDecodeWaves - 1][kMT * kNT][64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nkb = (int)(k / kBlock);
-  for (int i = t; i < nkb * kDecodeMaxM; i += 64 * kDecodeWaves) {
-    const int kb = i / kDecodeMaxM, r = i % kDecodeMaxM;
+  for (int i = t; i < nkb * kRows; i += 64 * kDecodeWaves) {
+    const int kb = i / kRows, r = i % kRows;
     as_t[kb][r] = r < m ? a_s[(int64_t)r * nkb + kb] : 0.0f;
   }
   __syncthreads();
 
-  const int64_t n0 = ((int64_t)blockIdx.x * kDecodeWaves + wave) * 16;
-  if (n0 >= n) return;                                  // whole wave past the edge
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * kNT;
   const int fr = lane & 15, fq = lane >> 4;
   const float *bs_row = b_s + (n0 / kBlock) * nkb;
+  const int kb_begin = wave * nkb / kDecodeWaves, kb_end = (wave + 1) * nkb / kDecodeWaves;
   // lane -> (row fr, bytes [16 fq, 16 fq + 16) and [64 + 16 fq, ...)) of a K block;
   // A and B use the same byte -> k assignment.
-  const uint8_t *b_src = b + min(n0 + fr, n - 1) * k + 16 * fq;
+  const uint8_t *b_src[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) b_src[nt] = b + min(n0 + 16 * nt + fr, n - 1) * k + 16 * fq;
   const uint8_t *a_src[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) a_src[mt] = a + min((int64_t)(16 * mt + fr), m - 1) * k + 16 * fq;
 
-  auto load_b = [&](int kb) {
-    const uint8_t *p = b_src + (int64_t)kb * kBlock;
-    const uint4 lo = *(const uint4 *)p, hi = *(const uint4 *)(p + 64);
-    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  };
-  auto load_a = [&](int mt, int kb) {
-    const uint8_t *p = a_src[mt] + (int64_t)kb * kBlock;
+  auto load_frag = [&](const uint8_t *row, int kb) {
+    const uint8_t *p = row + (int64_t)kb * kBlock;
     const uint4 lo = *(const uint4 *)p, hi = *(const uint4 *)(p + 64);
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
 
-  f32x4 acc[kMT];
+  f32x4 acc[kMT][kNT];
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  i32x8 bq[kDepth];
+  // ring of the B fragments of the next kDepth K blocks
+  i32x8 bq[kDepth][kNT];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
-    if (d < nkb) bq[d] = load_b(d);
+    if (kb_begin + d < kb_end)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) bq[d][nt] = load_frag(b_src[nt], kb_begin + d);
 
-  for (int kb0 = 0; kb0 < nkb; kb0 += kDepth) {
+  for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int kb = kb0 + d;
-      if (kb < nkb) {
-        const i32x8 bf = bq[d];
-        if (kb + kDepth < nkb) bq[d] = load_b(kb + kDepth);
+      if (kb < kb_end) {
+        i32x8 bf[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          bf[nt] = bq[d][nt];
+          if (kb + kDepth < kb_end) bq[d][nt] = load_frag(b_src[nt], kb + kDepth);
+        }
         const float sb = bs_row[kb];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           const f32x4 sa = *(const f32x4 *)&as_t[kb][16 * mt + 4 * fq];
-          const f32x4 p = mfma_e4m3_16x16x128(load_a(mt, kb), bf, f32x4{0.f, 0.f, 0.f, 0.f});
+          const i32x8 af = load_frag(a_src[mt], kb);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(p[e], sa[e] * sb, acc[mt][e]);
+          for (int nt = 0; nt < kNT; ++nt) {
+            const f32x4 p = mfma_e4m3_16x16x128(af, bf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[mt][nt][e] = __builtin_fmaf(p[e], sa[e] * sb, acc[mt][nt][e]);
+          }
         }
       }
     }
   }
 
-  const int64_t col = n0 + fr;
+  // waves 1..3 hand their partial sums to wave 0 through LDS
+  if (wave > 0) {
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t row = 16 * mt + 4 * fq + e;
-      if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][e]);
-    }
+      for (int nt = 0; nt < kNT; ++nt) red[wave - 1][mt * kNT + nt][lane] = acc[mt][nt];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kDecodeWaves - 1; ++w)
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const f32x4 o = red[w][mt * kNT + nt][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mt][nt][e] += o[e];
+      }
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int64_t col = n0 + 16 * nt + fr;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = 16 * mt + 4 * fq + e;
+        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][nt][e]);
+      }
+  }
 }
 
 }  // namespace
@@ -414,22 +453,22 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
     return hipGetLastError();
   }
   if (m <= kDecodeMaxM && k / kBlock <= kDecodeMaxKb) {
-    const dim3 grid((unsigned)((n + 16 * kDecodeWaves - 1) / (16 * kDecodeWaves))),
-        block(64 * kDecodeWaves);
-#define FP8BSQ_DECODE(MT)                                                                        \
+    const dim3 block(64 * kDecodeWaves);
+#define FP8BSQ_DECODE(MT, NT, D)                                                                 \
   do {                                                                                           \
+    const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)));                                  \
     if (c_bf16)                                                                                  \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT>), grid, block, 0, stream, a, a_s, b, \
-                         b_s, c, m, n, k);                                                       \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, NT, D>), grid, block, 0, stream, a,  \
+                         a_s, b, b_s, c, m, n, k);                                               \
     else                                                                                         \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT>), grid, block, 0, stream, a, a_s,  \
-                         b, b_s, c, m, n, k);                                                    \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, NT, D>), grid, block, 0, stream, a, \
+                         a_s, b, b_s, c, m, n, k);                                               \
   } while (0)
     switch ((m + 15) / 16) {
-      case 1: FP8BSQ_DECODE(1); break;
-      case 2: FP8BSQ_DECODE(2); break;
-      case 3: FP8BSQ_DECODE(3); break;
-      default: FP8BSQ_DECODE(4); break;
+      case 1: FP8BSQ_DECODE(1, 1, 8); break;
+      case 2: FP8BSQ_DECODE(2, 2, 4); break;
+      case 3: FP8BSQ_DECODE(3, 2, 4); break;
+      default: FP8BSQ_DECODE(4, 2, 4); break;
     }
 #undef FP8BSQ_DECODE
     return hipGetLastError();
