@@ -20,10 +20,19 @@ bounded sample of the same workload: the first ``--cpu-rows`` activation rows
 through act_quant and the GEMM, and the matching fraction of the weight through
 weight_dequant.
 
+``roofline.traffic`` is the GEMM's HBM traffic per launch measured with
+rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
+reads for a copy of known size), read from profiles/block_gemm_prefill_traffic.json;
+it is reported as null when the GEMM source has changed since those counters
+were taken.
+
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+       python bench.py --profile-workload NAME [--iters N]   (one kernel, for rocprofv3)
+       python bench.py --calibrate-copy                      (copy of known size, for rocprofv3)
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -47,10 +56,84 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--cpu-rows", type=int, default=512,
+    p.add_argument("--cpu-rows", type=int, default=4096,
                    help="activation rows in the CPU oracle sample (0 skips it)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--profile-workload", default=None,
+                   choices=["act_quant", "act_quant_ue8m0", "dequant", "dequant_ragged", "decode1",
+                            "decode8", "decode32", "decode64", "prefill1", "prefill2"],
+                   help="run only this workload's kernel --iters times (for rocprofv3)")
+    p.add_argument("--iters", type=int, default=20)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="copy 1 GiB once with torch (counter calibration under rocprofv3)")
     return p.parse_args()
+
+
+GEMM_SOURCE = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc", "block_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_gemm_prefill_traffic.json")
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    if it is missing or was taken on a different GEMM source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("block_gemm_hip_sha256") != source_hash(GEMM_SOURCE):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def profile_workload(name, iters):
+    """Run one workload's kernel `iters` times (inputs resident in HBM)."""
+    import torch
+
+    import fp8_block_scaled_quant_amd as fb
+    from inputs import gen
+
+    dev = torch.device("cuda:0")
+    if name.startswith("act_quant"):
+        x = gen.act_quant_workload()["x"].to(dev)
+        fmt = "ue8m0" if name.endswith("ue8m0") else None
+        run = lambda: fb.act_quant(x, 128, fmt)
+    elif name.startswith("dequant"):
+        d = gen.dequant_workload(n=18440 if name.endswith("ragged") else 18432)
+        w = torch.from_numpy(d["w"]).to(dev)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+        run = lambda: fb.weight_dequant(w, ws, 128, torch.bfloat16)
+    elif name.startswith("decode"):
+        d = gen.decode_gemm(int(name[len("decode"):]))
+        y, s = fb.act_quant(d["x"].to(dev))
+        w = torch.from_numpy(d["w"]).to(dev)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+        run = lambda: fb.fp8_gemm(y, s, w, ws, torch.bfloat16)
+    else:
+        d = gen.prefill_gemm(int(name[-1]))
+        y, s = fb.act_quant(d["x"].to(dev), 128, "ue8m0")
+        w = torch.from_numpy(d["w"]).to(dev)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+        run = lambda: fb.fp8_gemm(y, s, w, ws, torch.bfloat16)
+    for _ in range(iters):
+        run()
+    torch.cuda.synchronize()
+    print(f"ran {name} x{iters}", flush=True)
+
+
+def calibrate_copy():
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied 1073741824 bytes", flush=True)
 
 
 def cpu_baseline(x_bf16, w, ws, rows):
@@ -85,6 +168,12 @@ def cpu_baseline(x_bf16, w, ws, rows):
 
 def main():
     args = parse()
+    if args.profile_workload:
+        profile_workload(args.profile_workload, args.iters)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(every kernel here runs on a single device with no cross-GPU work).", file=sys.stderr)
@@ -166,7 +255,7 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gemm_tflops / PEAK_FP8_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "kernels": {
             "act_quant": {"us": aq_ms * 1e3, "GB/s": aq_gbs, "frac_hbm": aq_gbs / PEAK_HBM_GBS,
