@@ -242,17 +242,15 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto step = [&](int kb, int cur) {
+    const float sbv = bs_row[kb];   // scalar load, issued ahead of the wait below
     wait_dma_all();
     workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
     if (kb + 1 < nkb) issue(kb + 1, cur ^ 1);
-    const float sbv = bs_row[kb];
-    float sc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 v = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[i][e] = v[e] * sbv;
-    }
+    // Retire the scalar load now (the empty asm consumes its value): scalar and
+    // LDS results share one counter and the scalar one may return out of order,
+    // so while it is outstanding every LDS wait would have to be a full drain.
+    asm volatile("" ::"s"(sbv));
+    // fragment reads first: the first MFMA waits only for these
     i32x8 af[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -263,8 +261,14 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       const int r = wn + 16 * j + fr;
       return frag_from_lds(&sm.b[cur][r * kBlock], fq, r);
     };
-    // MFMA q = 4 j + i; its rescale runs two MFMAs later (ring of 3 partials).
     i32x8 bcur = read_b(0), bnext;
+    f32x4 sav[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+    // MFMA q = 4 j + i; its rescale runs two MFMAs later (ring of 3 partials).
+    // The row scales a_s * b_s are formed at their first use (q - 2 < 4), so
+    // their LDS reads never hold up the first MFMAs.
+    float sc[4][4];
     f32x4 part[3];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -275,6 +279,10 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
         part[q % 3] = mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
         if (q >= 2) {
           const int qp = q - 2, ip = qp % 4, jp = qp / 4;
+          if (qp < 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[ip][e] = sav[ip][e] * sbv;
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[ip][jp][e] = __builtin_fmaf(part[qp % 3][e], sc[ip][e], acc[ip][jp][e]);
