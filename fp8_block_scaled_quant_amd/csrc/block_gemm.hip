@@ -127,9 +127,10 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 //
 // Each wave's 128 columns lie inside one 128-row weight block, so b_s is one
 // scalar per wave and K block.  The per-K-block rescale (4 FMAs per MFMA) is
-// software-pipelined by hand two MFMAs behind the MFMA that produced its
-// partial, which keeps only three partials live; the scheduler would otherwise
-// hoist all 32 MFMAs of a K block and run out of registers.
+// software-pipelined by hand three MFMAs behind the MFMA that produced its
+// partial, which keeps four partials live and lets the FMAs read them without
+// hazard wait states; the scheduler would otherwise hoist all 32 MFMAs of a K
+// block and run out of registers.
 //
 // LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r is stored at
 // slot c ^ swz(r), so the 16 rows a fragment read touches hit distinct banks.
@@ -265,38 +266,38 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     f32x4 sav[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
-    // MFMA q = 4 j + i; its rescale runs two MFMAs later (ring of 3 partials).
+    // MFMA q = 4 j + i; its rescale runs three MFMAs later (ring of 4 partials).
     // The row scales a_s * b_s are formed at their first use (q - 2 < 4), so
     // their LDS reads never hold up the first MFMAs.
     float sc[4][4];
-    f32x4 part[3];
+    f32x4 part[4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j + 1 < 8) bnext = read_b(j + 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = 4 * j + i;
-        part[q % 3] = mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
-        if (q >= 2) {
-          const int qp = q - 2, ip = qp % 4, jp = qp / 4;
+        part[q % 4] = mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (q >= 3) {
+          const int qp = q - 3, ip = qp % 4, jp = qp / 4;
           if (qp < 4) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sc[ip][e] = sav[ip][e] * sbv;
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[ip][jp][e] = __builtin_fmaf(part[qp % 3][e], sc[ip][e], acc[ip][jp][e]);
+            acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], sc[ip][e], acc[ip][jp][e]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (j + 1 < 8) bcur = bnext;
     }
 #pragma unroll
-    for (int qp = 30; qp < 32; ++qp) {
+    for (int qp = 29; qp < 32; ++qp) {
       const int ip = qp % 4, jp = qp / 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc[ip][jp][e] = __builtin_fmaf(part[qp % 3][e], sc[ip][e], acc[ip][jp][e]);
+        acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], sc[ip][e], acc[ip][jp][e]);
     }
   };
 
