@@ -11,6 +11,10 @@ the order activations, then weight codes, then weight scales):
 * weight codes: uniform over the 254 finite E4M3 codes (0x7F and 0xFF, the two
   NaNs, excluded; +-0 and subnormals included).
 * block scales: float32(2 ** U[lo, hi]) (log-uniform).
+* weights to quantize: ``standard_normal`` fp32 times a per-128x128-tile
+  magnitude 2 ** U[-10, 0]; 0.01% of the elements multiplied by 100; one
+  all-zero tile in every 8th row of tiles (tile column U[0, ceil(K/128)));
+  then cast to bf16.
 
 Nothing here is part of the quantization method.
 """
@@ -27,6 +31,8 @@ SEED_DEQUANT = 2
 SEED_DEQUANT_RAGGED = 12
 SEED_DECODE_BASE = 3      # + M
 SEED_PREFILL = (4, 5)     # shape 1, shape 2
+SEED_WEIGHT_QUANT = 6
+SEED_WEIGHT_QUANT_RAGGED = 16
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -140,6 +146,26 @@ def prefill_gemm(shape: int = 1, m: int = 8192):
     w = weight_codes(rng, n, k)
     ws = log_uniform_scales(rng, scale_grid(n, k), -14, -2)
     return {"x": x, "w": w, "w_s": ws, "scale_fmt": "ue8m0", "out": "bf16"}
+
+
+def weight_quant_workload(n: int = 18432, k: int = 7168, seed: int = None, dtype: str = "bf16"):
+    """Weights [n, k] to quantize per 128 x 128 tile (``dtype`` 'bf16' or 'f32')."""
+    if seed is None:
+        seed = SEED_WEIGHT_QUANT if n % BLOCK == 0 and k % BLOCK == 0 else SEED_WEIGHT_QUANT_RAGGED
+    rng = rng_for(seed)
+    gm, gn = scale_grid(n, k)
+    w = normal_f32(rng, (n, k))
+    mag = log_uniform_scales(rng, (gm, gn), -10, 0)
+    w *= np.repeat(np.repeat(mag, BLOCK, 0), BLOCK, 1)[:n, :k]
+    add_outliers(rng, w, frac=1e-4)
+    for i in range(0, gm, 8):
+        j = int(rng.integers(0, gn))
+        w[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK] = 0.0
+    if dtype == "bf16":
+        return {"w": to_bf16(w)}
+    if dtype == "f32":
+        return {"w": torch.from_numpy(w)}
+    raise ValueError(dtype)
 
 
 def custom_gemm(seed: int, m: int, n: int, k: int, dtype: str = "bf16", outliers: bool = False,

@@ -12,6 +12,7 @@ It is a plain, slow, obviously-correct statement of what the method computes:
                          encode with saturation at 448.
 * ``act_quant``       -- dynamic 1x128 activation quantization.
 * ``weight_dequant``  -- 128x128 block-scaled weight dequantization.
+* ``weight_quant``    -- 128x128 block weight quantization (its inverse).
 * ``fp8_gemm``        -- the block-scaled FP8 GEMM, each 128-wide K slice's
                          partial sum scaled and accumulated, in float64, plus the
                          per-element error bound GPU results are held to.
@@ -26,4 +27,5 @@ H800 hardware): those are "parity unpinned" and nothing here computes them.
 from . import e4m3  # noqa: F401
 from .act_quant import act_quant  # noqa: F401
 from .weight_dequant import weight_dequant, f32_to_bf16_bits, bf16_bits_to_f32  # noqa: F401
+from .weight_quant import weight_quant  # noqa: F401
 from .fp8_gemm import fp8_gemm, dequantized_operands, gemm_tolerance, gemm_check  # noqa: F401

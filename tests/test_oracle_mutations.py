@@ -234,3 +234,79 @@ def test_gemm_reversed_k_in_one_operand():
 def test_gemm_decode_sign_lost(monkeypatch):
     monkeypatch.setattr(e4m3, "decode", lambda c: np.abs(e4m3.DECODE[np.asarray(c)]))
     assert _gemm_any_fails(oracle.fp8_gemm)
+
+
+# --------------------------------------------------------------- weight quant
+
+from tests import test_oracle_weight_quant as T_wq  # noqa: E402
+
+
+def _wq_any_fails(weight_quant):
+    checks = [
+        (T_wq.check_identical_rows_match_act_quant, (weight_quant, None)),
+        (T_wq.check_identical_rows_match_act_quant, (weight_quant, "ue8m0")),
+        (T_wq.check_zero_tile, (weight_quant,)),
+        (T_wq.check_tile_max_hits_448, (weight_quant,)),
+        (T_wq.check_grid_and_edge_tiles, (weight_quant,)),
+        (T_wq.check_round_trip, (weight_quant, None)),
+        (T_wq.check_round_trip, (weight_quant, "ue8m0")),
+        (T_wq.check_vs_torch, (weight_quant, T_wq.small_weights(), None)),
+        (T_wq.check_vs_torch, (weight_quant, T_wq.small_weights(), "ue8m0")),
+        (T_wq.check_exact_quotients, (weight_quant, None, 3)),
+        (T_wq.check_exact_quotients, (weight_quant, "ue8m0", 3)),
+    ]
+    return any(_fails(f, *a) for f, a in checks)
+
+
+def _wq_variant(amax_of=None, quotient=None, clamp_after_div=False, ue8m0_down=False, tiles_of=None):
+    """The oracle's weight_quant with one step replaced."""
+    def wq(x, block_size=128, scale_fmt=None):
+        m, n = x.shape
+        bs = block_size
+        gm, gn = -(-m // bs), -(-n // bs)
+        xp = np.zeros((gm * bs, gn * bs), dtype=np.float32)
+        xp[:m, :n] = x
+        tiles = tiles_of(xp, gm, gn, bs) if tiles_of else xp.reshape(gm, bs, gn, bs)
+        amax = amax_of(tiles) if amax_of else np.max(np.abs(tiles), axis=(1, 3))
+        if clamp_after_div:
+            s = np.maximum((amax / np.float32(448)).astype(np.float32), np.float32(1e-4))
+        else:
+            s = (np.maximum(amax, np.float32(1e-4)) / np.float32(448)).astype(np.float32)
+        if scale_fmt == "ue8m0":
+            if ue8m0_down:
+                s = np.ldexp(np.float32(1.0), np.frexp(s.astype(np.float64))[1] - 1).astype(np.float32)
+            else:
+                s = wq_mod._ue8m0_round_up(s)
+        sb = s[:, None, :, None]
+        q = quotient(tiles, sb) if quotient else (tiles / sb).astype(np.float32)
+        if tiles_of:   # back to the padded matrix's element order
+            q = q.transpose(0, 2, 1, 3)
+        codes = e4m3.encode(q).reshape(gm * bs, gn * bs)[:m, :n]
+        return np.ascontiguousarray(codes), s
+    return wq
+
+
+wq_mod = importlib.import_module("oracle.weight_quant")
+
+
+def test_wq_variant_harness_is_faithful():
+    """With nothing replaced, the variant builder reproduces the oracle."""
+    x = T_wq.small_weights(300, 520, seed=31)
+    for fmt in (None, "ue8m0"):
+        q, s = _wq_variant()(x, 128, fmt)
+        q0, s0 = oracle.weight_quant(x, 128, fmt)
+        assert np.array_equal(q, q0) and np.array_equal(s, s0)
+
+
+@pytest.mark.parametrize("name, mutant", [
+    ("amax of the tile's first row only", _wq_variant(amax_of=lambda t: np.max(np.abs(t[:, :1]), axis=(1, 3)))),
+    ("signed max instead of magnitude", _wq_variant(amax_of=lambda t: np.max(t, axis=(1, 3)))),
+    ("clamp applied to the scale", _wq_variant(clamp_after_div=True)),
+    ("multiply by fl32(1/s)", _wq_variant(quotient=lambda t, sb: (t * (np.float32(1) / sb).astype(np.float32)).astype(np.float32))),
+    ("ue8m0 rounded down", _wq_variant(ue8m0_down=True)),
+    # contiguous runs of 16384 elements taken as the tiles (a reshape slip)
+    ("16384-element strips instead of 128 x 128 tiles",
+     _wq_variant(tiles_of=lambda xp, gm, gn, bs: xp.reshape(gm, gn, bs, bs).transpose(0, 2, 1, 3))),
+])
+def test_weight_quant_mutants_caught(name, mutant):
+    assert _wq_any_fails(mutant), name
