@@ -11,6 +11,10 @@ Functions follow the call shapes the pages give:
 * ``act_quant(x, block_size=128, scale_fmt=None) -> (y, s)``
 * ``weight_dequant(x, s, block_size=128, out_dtype=torch.float32) -> y``
 * ``fp8_gemm(a, a_s, b, b_s, out_dtype=torch.bfloat16) -> c``
+
+and, producing the GEMM's weight operand,
+
+* ``weight_quant(w, block_size=128, scale_fmt=None) -> (y, s)``
 """
 
 import ctypes
@@ -19,7 +23,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["act_quant", "weight_dequant", "fp8_gemm", "Fp8Error", "library_path", "load_library"]
+__all__ = ["act_quant", "weight_dequant", "weight_quant", "fp8_gemm", "Fp8Error", "library_path",
+           "load_library"]
 
 Fp8Error = _lib.Fp8Error
 library_path = _lib.library_path
@@ -99,6 +104,31 @@ def weight_dequant(x: torch.Tensor, s: torch.Tensor, block_size: int = 128,
             ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(s.data_ptr()), m, n, block_size,
             ctypes.c_void_p(y.data_ptr()), _DTYPE[out_dtype], _stream_handle(x)))
     return y
+
+
+def weight_quant(w: torch.Tensor, block_size: int = 128, scale_fmt=None):
+    """Quantize a 2-D weight per block_size x block_size tile.
+
+    ``w`` is a contiguous bf16 or fp32 CUDA tensor [M, N] (any M, N >= 1).
+    Returns ``y`` (float8_e4m3fn [M, N]) and ``s`` (float32
+    [ceil(M/bs), ceil(N/bs)]), the operands ``weight_dequant`` and ``fp8_gemm``
+    take.
+    """
+    _require_gpu(w)
+    if w.dtype not in _DTYPE:
+        raise TypeError("weight_quant takes bf16 or fp32 input")
+    if w.dim() != 2:
+        raise ValueError("weight must be 2-D")
+    if scale_fmt not in _SCALE_FMT:
+        raise ValueError(f"unknown scale_fmt {scale_fmt!r}")
+    m, n = w.shape
+    y = torch.empty((m, n), dtype=torch.uint8, device=w.device)
+    s = torch.empty((-(-m // block_size), -(-n // block_size)), dtype=torch.float32, device=w.device)
+    if m and n:
+        _lib.check(_lib.lib().fp8_weight_quant(
+            ctypes.c_void_p(w.data_ptr()), _DTYPE[w.dtype], m, n, block_size, _SCALE_FMT[scale_fmt],
+            ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(s.data_ptr()), _stream_handle(w)))
+    return y.view(torch.float8_e4m3fn), s
 
 
 def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfp8bsq.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["abi.cpp", "act_quant.hip", "weight_dequant.hip", "block_gemm.hip"]
+SOURCES = ["abi.cpp", "act_quant.hip", "weight_dequant.hip", "weight_quant.hip", "block_gemm.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

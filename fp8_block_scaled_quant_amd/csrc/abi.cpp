@@ -47,6 +47,21 @@ int fp8_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, i
                                                      (hipStream_t)hip_stream));
 }
 
+int fp8_weight_quant(const void *x, int x_dtype, int64_t m, int64_t n, int block_size,
+                     int scale_fmt, uint8_t *y, float *s, void *hip_stream) {
+  if (!x || !y || !s) return FP8BSQ_EINVAL;
+  if (m <= 0 || n <= 0) return FP8BSQ_EINVAL;
+  if (x_dtype != FP8BSQ_F32 && x_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
+  if (scale_fmt != FP8BSQ_SCALE_NONE && scale_fmt != FP8BSQ_SCALE_UE8M0) return FP8BSQ_EINVAL;
+  if (block_size != 128) return FP8BSQ_EUNSUPPORTED;
+  if (!aligned(x, x_dtype == FP8BSQ_F32 ? 4 : 2) || !aligned(s, 4)) return FP8BSQ_EALIGN;
+  if (m >= kMaxDim || n >= kMaxDim || m * n >= ((int64_t)1 << 50)) return FP8BSQ_ERANGE;
+  if ((m + 127) / 128 > 65535) return FP8BSQ_ERANGE;   // grid.y
+  return launch_status(fp8bsq::launch_weight_quant(x, x_dtype == FP8BSQ_BF16, m, n,
+                                                   scale_fmt == FP8BSQ_SCALE_UE8M0, y, s,
+                                                   (hipStream_t)hip_stream));
+}
+
 int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
                    void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
   if (!a || !a_s || !b || !b_s || !c) return FP8BSQ_EINVAL;

@@ -16,6 +16,10 @@ hipError_t launch_act_quant(const void *x, bool x_bf16, int64_t nblocks, bool ue
 hipError_t launch_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, void *y,
                                  bool y_bf16, hipStream_t stream);
 
+// x: [m, n] bf16 or fp32; y: [m, n] codes; s: [ceil(m/128), ceil(n/128)] scales.
+hipError_t launch_weight_quant(const void *x, bool x_bf16, int64_t m, int64_t n, bool ue8m0,
+                               uint8_t *y, float *s, hipStream_t stream);
+
 // C[m, n] = block-scaled A[m, k] . B[n, k]^T.
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,

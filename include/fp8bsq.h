@@ -1,7 +1,8 @@
 /*
  * fp8bsq.h -- C ABI of the block-scaled FP8 library for AMD Instinct MI355X
  * (gfx950): dynamic 1x128 activation quantization, 128x128 block-scaled
- * weight dequantization, and the block-scaled FP8 E4M3 GEMM those two feed.
+ * weight dequantization, the block-scaled FP8 E4M3 GEMM those two feed, and
+ * the 128x128 weight quantization that produces the GEMM's weight operand.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -96,6 +97,38 @@ FP8BSQ_API int fp8_act_quant(const void *x, int x_dtype, int64_t rows, int64_t k
  */
 FP8BSQ_API int fp8_weight_dequant(const uint8_t *x, const float *s, int64_t m, int64_t n, int block_size,
                        void *y, int y_dtype, void *hip_stream);
+
+/*
+ * fp8_weight_quant -- 128x128 block weight quantization (fp8_weight_dequant's
+ * inverse).
+ *
+ * The storage format is defined on the page "DeepSeek-V3 quantization_config
+ * Parameters Explained", section "The weight_block_size Parameter" (E4M3
+ * codes in 128 x 128 blocks, each with its own inverse scale,
+ * weight_scale_inv) and on "How weight_dequant Handles Per-Block Scaling in
+ * DeepSeek-V3 FP8 GEMM", sections "Per-Block Scaling Architecture" and "Grid
+ * Mapping and Scale Lookup" (the scale grid and y = x * s).  The pages give
+ * no formula for producing the codes; this entry point applies the
+ * activation rule of fp8_act_quant to each tile: amax = max |x| over the
+ * tile's elements clamped to at least 1e-4, s = fl32(amax / 448) (or the
+ * smallest power of two >= that under FP8BSQ_SCALE_UE8M0),
+ * y = RNE_E4M3(fl32(x / s)) saturating at +-448, sign kept on zero.
+ *
+ *   x          [m, n] weights, dtype x_dtype (FP8BSQ_F32 or FP8BSQ_BF16),
+ *              aligned to its element size.
+ *   m, n       >= 1; need not be multiples of block_size (edge tiles use
+ *              their valid elements only); m <= 65535 * 128 (else
+ *              FP8BSQ_ERANGE).
+ *   y          [m, n] E4M3 codes out.
+ *   s          [ceil(m / block_size), ceil(n / block_size)] FP32 scales out,
+ *              row-major, 4-byte aligned; fp8_weight_dequant(y, s) maps the
+ *              codes back to within half an E4M3 ulp of x / s, times s.
+ *
+ * Results are bit-identical to the CPU oracle for finite x.  Inputs with
+ * n % 8 == 0, 16-byte-aligned x and 8-byte-aligned y take the vectorized path.
+ */
+FP8BSQ_API int fp8_weight_quant(const void *x, int x_dtype, int64_t m, int64_t n, int block_size,
+                     int scale_fmt, uint8_t *y, float *s, void *hip_stream);
 
 /*
  * fp8_block_gemm -- block-scaled FP8 GEMM, C = A . B^T.

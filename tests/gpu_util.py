@@ -63,6 +63,31 @@ def act_quant(x: torch.Tensor, scale_fmt=None):
     return codes, scales
 
 
+def weight_quant(w: torch.Tensor, scale_fmt=None, offset: int = 0):
+    """w: CUDA bf16/fp32 [m, n] (moved to a buffer offset by `offset` elements).
+
+    Returns (codes uint8 numpy [m, n], scales fp32 numpy grid).
+    """
+    m, n = w.shape
+    esz = w.element_size()
+    wd = Guarded(m * n * esz, offset=offset * esz)
+    wd.payload().copy_(w.contiguous().view(torch.uint8).reshape(-1))
+    gm, gn = -(-m // 128), -(-n // 128)
+    y = Guarded(m * n, offset=offset)
+    s = Guarded(gm * gn * 4)
+    dt = _lib.BF16 if w.dtype == torch.bfloat16 else _lib.F32
+    fmt = _lib.SCALE_UE8M0 if scale_fmt == "ue8m0" else _lib.SCALE_NONE
+    st = _lib.lib().fp8_weight_quant(ctypes.c_void_p(wd.ptr), dt, m, n, 128, fmt,
+                                     ctypes.c_void_p(y.ptr), ctypes.c_void_p(s.ptr), stream())
+    assert st == _lib.OK, st
+    torch.cuda.synchronize()
+    y.check_guards()
+    s.check_guards()
+    wd.check_guards()
+    return (y.payload().cpu().numpy().reshape(m, n),
+            s.payload().cpu().numpy().view(np.float32).reshape(gm, gn))
+
+
 def weight_dequant(w: np.ndarray, s: np.ndarray, out: str = "bf16", offset: int = 0):
     """w uint8 [m, n], s fp32 grid.  Returns bf16 bits (uint16) or fp32 numpy."""
     m, n = w.shape

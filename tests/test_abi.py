@@ -94,3 +94,20 @@ def test_block_gemm_validation(lib):
     assert f(P, P, P + 8, P, P, 1, 16, 16, 128, None) == _lib.EALIGN
     assert f(P, P, P, P, P + 2, 1, 16, 16, 128, None) == _lib.EALIGN
     assert f(P, P, P, P, P, 1, 1 << 40, 16, 128, None) == _lib.ERANGE
+
+
+def test_weight_quant_validation(lib):
+    f = lib.fp8_weight_quant
+    assert f(None, 1, 8, 8, 128, 0, P, P, None) == _lib.EINVAL
+    assert f(P, 1, 8, 8, 128, 0, None, P, None) == _lib.EINVAL
+    assert f(P, 1, 8, 8, 128, 0, P, None, None) == _lib.EINVAL
+    assert f(P, 1, 0, 8, 128, 0, P, P, None) == _lib.EINVAL
+    assert f(P, 1, 8, -1, 128, 0, P, P, None) == _lib.EINVAL
+    assert f(P, 2, 8, 8, 128, 0, P, P, None) == _lib.EINVAL
+    assert f(P, 1, 8, 8, 128, 3, P, P, None) == _lib.EINVAL
+    assert f(P, 1, 8, 8, 64, 0, P, P, None) == _lib.EUNSUPPORTED
+    assert f(P + 1, 1, 8, 8, 128, 0, P, P, None) == _lib.EALIGN
+    assert f(P + 2, 0, 8, 8, 128, 0, P, P, None) == _lib.EALIGN
+    assert f(P, 1, 8, 8, 128, 0, P, P + 2, None) == _lib.EALIGN
+    assert f(P, 1, 1 << 31, 8, 128, 0, P, P, None) == _lib.ERANGE
+    assert f(P, 1, 65536 * 128, 8, 128, 0, P, P, None) == _lib.ERANGE
