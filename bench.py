@@ -60,8 +60,9 @@ def parse():
                    help="activation rows in the CPU oracle sample (0 skips it)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--profile-workload", default=None,
-                   choices=["act_quant", "act_quant_ue8m0", "dequant", "dequant_ragged", "decode1",
-                            "decode8", "decode32", "decode64", "prefill1", "prefill2"],
+                   choices=["act_quant", "act_quant_ue8m0", "dequant", "dequant_ragged", "weight_quant",
+                            "weight_quant_ue8m0", "decode1", "decode8", "decode32", "decode64",
+                            "prefill1", "prefill2"],
                    help="run only this workload's kernel --iters times (for rocprofv3)")
     p.add_argument("--iters", type=int, default=20)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -108,6 +109,10 @@ def profile_workload(name, iters):
         w = torch.from_numpy(d["w"]).to(dev)
         ws = torch.from_numpy(d["w_s"]).to(dev)
         run = lambda: fb.weight_dequant(w, ws, 128, torch.bfloat16)
+    elif name.startswith("weight_quant"):
+        w = gen.weight_quant_workload()["w"].to(dev)
+        fmt = "ue8m0" if name.endswith("ue8m0") else None
+        run = lambda: fb.weight_quant(w, 128, fmt)
     elif name.startswith("decode"):
         d = gen.decode_gemm(int(name[len("decode"):]))
         y, s = fb.act_quant(d["x"].to(dev))

@@ -15,6 +15,11 @@ Functions follow the call shapes the pages give:
 and, producing the GEMM's weight operand,
 
 * ``weight_quant(w, block_size=128, scale_fmt=None) -> (y, s)``
+
+and a linear layer's forward product in one call (act_quant, then fp8_gemm;
+a single kernel for bf16 decode batches of up to 2 rows),
+
+* ``act_quant_gemm(x, b, b_s, scale_fmt=None, out_dtype=torch.bfloat16) -> (c, y, s)``
 """
 
 import ctypes
@@ -23,8 +28,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["act_quant", "weight_dequant", "weight_quant", "fp8_gemm", "Fp8Error", "library_path",
-           "load_library"]
+__all__ = ["act_quant", "weight_dequant", "weight_quant", "fp8_gemm", "act_quant_gemm", "Fp8Error",
+           "library_path", "load_library"]
 
 Fp8Error = _lib.Fp8Error
 library_path = _lib.library_path
@@ -162,3 +167,41 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Ten
             ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),
             ctypes.c_void_p(c.data_ptr()), _DTYPE[out_dtype], m, n, k, _stream_handle(a)))
     return c
+
+
+def act_quant_gemm(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, scale_fmt=None,
+                   out_dtype: torch.dtype = torch.bfloat16):
+    """``act_quant(x)`` then ``fp8_gemm`` with the weight ``b`` [N, K] / ``b_s``.
+
+    Returns ``(c [..., N], y, s)`` where ``(y, s)`` are act_quant's outputs,
+    bit-identical to calling ``act_quant`` separately.
+    """
+    b = _codes(b)
+    _require_gpu(x, b, b_s)
+    if x.dtype not in _DTYPE:
+        raise TypeError("act_quant_gemm takes bf16 or fp32 activations")
+    if scale_fmt not in _SCALE_FMT:
+        raise ValueError(f"unknown scale_fmt {scale_fmt!r}")
+    if out_dtype not in _DTYPE:
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if b_s.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    k = x.shape[-1]
+    if k % 128 != 0:
+        raise ValueError("K must be a multiple of 128")
+    if b.dim() != 2 or b.shape[1] != k:
+        raise ValueError("b must be [N, K] with x's K")
+    n = b.shape[0]
+    if tuple(b_s.shape) != (-(-n // 128), k // 128):
+        raise ValueError("b_s must be [ceil(N/128), K/128]")
+    m = x.numel() // k if k else 0
+    y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty(x.shape[:-1] + (k // 128,), dtype=torch.float32, device=x.device)
+    c = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=out_dtype, device=x.device)
+    if m and n:
+        _lib.check(_lib.lib().fp8_act_quant_gemm(
+            ctypes.c_void_p(x.data_ptr()), _DTYPE[x.dtype], _SCALE_FMT[scale_fmt],
+            ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),
+            ctypes.c_void_p(c.data_ptr()), _DTYPE[out_dtype], m, n, k,
+            ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(s.data_ptr()), _stream_handle(x)))
+    return c, y.view(torch.float8_e4m3fn), s

@@ -16,8 +16,8 @@
 // same lane/byte -> k assignment, so the product is the block's full dot
 // product whatever order the hardware pairs the bytes in.  The 16x16 FP32
 // result sits in lane l as column (l % 16), rows 4 * (l / 16) + 0..3.
-#include "device_common.h"
 #include "launch.h"
+#include "quant_common.h"
 
 namespace fp8bsq {
 namespace {
@@ -334,19 +334,69 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 // MFMA tiles cover the activation rows.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4, kDecodeMaxM = 64, kDecodeMaxKb = 160;
+// Activations quantized inside the decode kernel (fused act_quant) for up to
+// this many rows: every workgroup quantizes all of them, so the redundant work
+// grows with m: at m = 1 the one launch beats act_quant + GEMM by about 5%,
+// at m = 2 they tie, and at m = 4 two launches are faster.
+constexpr int kFusedMaxM = 2;
 
-template <bool kBf16Out, int kMT, int kNT, int kDepth>
+// Fused prologue: quantize x [m, k] bf16 (m <= kFusedMaxM) per 1 x 128 block
+// exactly as the act_quant kernel does -- sixteen lanes per block, 8 elements
+// each, amax over the 16-lane row, the same scale and quotient arithmetic --
+// into LDS codes aq [m][k] and scales as_t [kb][row].  Workgroup 0 also writes
+// the codes and scales to a_q / a_s_out, bit-identical to fp8_act_quant.
+template <int kRows>
+__device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int m, int nkb,
+                                                bool ue8m0, uint8_t *aq, float (*as_t)[kRows],
+                                                uint8_t *__restrict__ a_q,
+                                                float *__restrict__ a_s_out, bool publish) {
+  const int t = threadIdx.x, row16 = t >> 4, sub = t & 15;
+  const int nblocks = m * nkb;                     // blocks of the flat [m * nkb, 128] sequence
+  // the sixteen lanes of a block share its loop trip count, as the row
+  // reduction needs
+  for (int blk = row16; blk < nblocks; blk += 64 * kDecodeWaves / 16) {
+    const u32x4 v = x[(int64_t)blk * 16 + sub];
+    u16x2 m2 = {0, 0};
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
+    const uint32_t amax = row_max_u32((uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16);
+    float sc, r;
+    block_scale_fast(amax, ue8m0, sc, r);
+    const u32x2 codes = encode_chunk_bf16(v, sc, r);
+    *(u32x2 *)(aq + (int64_t)blk * kBlock + 8 * sub) = codes;
+    const int row = blk / nkb, kb = blk % nkb;
+    if (sub == 0) as_t[kb][row] = sc;
+    if (publish) {
+      *(u32x2 *)(a_q + (int64_t)blk * kBlock + 8 * sub) = codes;
+      if (sub == 0) a_s_out[blk] = sc;
+    }
+  }
+}
+
+template <bool kBf16Out, int kMT, int kNT, int kDepth, bool kFuseQ = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
-    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k) {
+    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
+    bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr, float *__restrict__ a_s_out = nullptr) {
   constexpr int kRows = 16 * kMT;
   __shared__ float as_t[kDecodeMaxKb][kRows];   // [kb][row], zero-padded rows
   __shared__ f32x4 red[kDecodeWaves - 1][kMT * kNT][64];
+  extern __shared__ __attribute__((aligned(16))) uint8_t aq[];   // fused: codes [m][k]
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nkb = (int)(k / kBlock);
-  for (int i = t; i < nkb * kRows; i += 64 * kDecodeWaves) {
-    const int kb = i / kRows, r = i % kRows;
-    as_t[kb][r] = r < m ? a_s[(int64_t)r * nkb + kb] : 0.0f;
+  if constexpr (kFuseQ) {
+    // `a` holds the bf16 activations; rows m..kRows-1 of the scales stay 0
+    for (int i = t; i < nkb * kRows; i += 64 * kDecodeWaves) as_t[i / kRows][i % kRows] = 0.0f;
+    __syncthreads();
+    fused_act_quant<kRows>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q, a_s_out,
+                           blockIdx.x == 0);
+  } else {
+    for (int i = t; i < nkb * kRows; i += 64 * kDecodeWaves) {
+      const int kb = i / kRows, r = i % kRows;
+      as_t[kb][r] = r < m ? a_s[(int64_t)r * nkb + kb] : 0.0f;
+    }
   }
   __syncthreads();
 
@@ -362,6 +412,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
   const uint8_t *a_src[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) a_src[mt] = a + min((int64_t)(16 * mt + fr), m - 1) * k + 16 * fq;
+  // fused: rows past m are zero fragments, the others come from LDS
+  const bool a_row_live = fr < m;
+  const uint8_t *a_lds = aq + (int64_t)(a_row_live ? fr : 0) * k + 16 * fq;
 
   auto load_frag = [&](const uint8_t *row, int kb) {
     const uint8_t *p = row + (int64_t)kb * kBlock;
@@ -398,7 +451,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           const f32x4 sa = *(const f32x4 *)&as_t[kb][16 * mt + 4 * fq];
-          const i32x8 af = load_frag(a_src[mt], kb);
+          i32x8 af;
+          if constexpr (kFuseQ) {
+            af = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (a_row_live) {
+              const uint4 lo = *(const uint4 *)(a_lds + (int64_t)kb * kBlock);
+              const uint4 hi = *(const uint4 *)(a_lds + (int64_t)kb * kBlock + 64);
+              af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+          } else {
+            af = load_frag(a_src[mt], kb);
+          }
 #pragma unroll
           for (int nt = 0; nt < kNT; ++nt) {
             const f32x4 p = mfma_e4m3_16x16x128(af, bf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -490,6 +553,24 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
     hipLaunchKernelGGL(block_gemm_simple_kernel<false>, grid, block, 0, stream, a, a_s, b, b_s, c,
                        m, n, k);
   return hipGetLastError();
+}
+
+hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t *b,
+                                      const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                                      int64_t k, uint8_t *a_q, float *a_s, hipStream_t stream) {
+  const dim3 grid((unsigned)((n + 15) / 16)), block(64 * kDecodeWaves);
+  const size_t lds = (size_t)(m * k);
+  if (c_bf16)
+    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, 1, 8, true>), grid, block, lds, stream,
+                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, ue8m0, a_q, a_s);
+  else
+    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, 1, 8, true>), grid, block, lds, stream,
+                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, ue8m0, a_q, a_s);
+  return hipGetLastError();
+}
+
+bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k) {
+  return x_bf16 && m <= kFusedMaxM && k / kBlock <= kDecodeMaxKb;
 }
 
 }  // namespace fp8bsq

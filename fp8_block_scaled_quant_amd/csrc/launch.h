@@ -25,4 +25,12 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream);
 
+// Fused act_quant + decode GEMM (bf16 x [m, k], m small enough for
+// act_quant_gemm_fusable): C = Q(x) . B^T; a_q / a_s receive act_quant's codes
+// and scales.
+hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t *b,
+                                      const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                                      int64_t k, uint8_t *a_q, float *a_s, hipStream_t stream);
+bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k);
+
 }  // namespace fp8bsq

@@ -133,5 +133,38 @@ def block_gemm(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray, o
     return raw.view(np.float32).reshape(m, n).astype(np.float64)
 
 
+def act_quant_gemm(x: torch.Tensor, b: np.ndarray, b_s: np.ndarray, scale_fmt=None, out: str = "bf16"):
+    """Fused entry point.  x: CUDA bf16/fp32 [m, k].
+
+    Returns (C float64 numpy, codes uint8 numpy, scales fp32 numpy).
+    """
+    dev = device()
+    m, k = x.shape
+    n = b.shape[0]
+    bd = torch.from_numpy(b).to(dev)
+    bsd = torch.from_numpy(b_s).to(dev)
+    esz = 2 if out == "bf16" else 4
+    c = Guarded(m * n * esz)
+    y = Guarded(m * k)
+    s = Guarded(m * (k // 128) * 4)
+    dt = _lib.BF16 if x.dtype == torch.bfloat16 else _lib.F32
+    fmt = _lib.SCALE_UE8M0 if scale_fmt == "ue8m0" else _lib.SCALE_NONE
+    st = _lib.lib().fp8_act_quant_gemm(ctypes.c_void_p(x.data_ptr()), dt, fmt,
+                                       ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(bsd.data_ptr()),
+                                       ctypes.c_void_p(c.ptr), _lib.BF16 if out == "bf16" else _lib.F32,
+                                       m, n, k, ctypes.c_void_p(y.ptr), ctypes.c_void_p(s.ptr), stream())
+    assert st == _lib.OK, st
+    torch.cuda.synchronize()
+    for g in (c, y, s):
+        g.check_guards()
+    raw = c.payload().cpu().numpy()
+    if out == "bf16":
+        got = ((raw.view(np.uint16).reshape(m, n).astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    else:
+        got = raw.view(np.float32).reshape(m, n).astype(np.float64)
+    return (got, y.payload().cpu().numpy().reshape(m, k),
+            s.payload().cpu().numpy().view(np.float32).reshape(m, k // 128))
+
+
 def announce(msg: str):
     print(f"[gpu-test] {msg}", flush=True)

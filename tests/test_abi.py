@@ -111,3 +111,29 @@ def test_weight_quant_validation(lib):
     assert f(P, 1, 8, 8, 128, 0, P, P + 2, None) == _lib.EALIGN
     assert f(P, 1, 1 << 31, 8, 128, 0, P, P, None) == _lib.ERANGE
     assert f(P, 1, 65536 * 128, 8, 128, 0, P, P, None) == _lib.ERANGE
+
+
+def test_act_quant_gemm_validation(lib):
+    f = lib.fp8_act_quant_gemm
+    ok = (P, 1, 0, P, P, P, 1, 4, 256, 512, P, P, None)
+
+    def call(**kw):
+        args = list(ok)
+        for i, v in kw.items():
+            args[int(i[1:])] = v
+        return f(*args)
+
+    assert call(a0=None) == _lib.EINVAL
+    assert call(a3=None) == _lib.EINVAL
+    assert call(a10=None) == _lib.EINVAL
+    assert call(a11=None) == _lib.EINVAL
+    assert call(a7=0) == _lib.EINVAL
+    assert call(a1=5) == _lib.EINVAL
+    assert call(a2=2) == _lib.EINVAL
+    assert call(a6=9) == _lib.EINVAL
+    assert call(a9=200) == _lib.ESHAPE
+    assert call(a0=P + 8) == _lib.EALIGN
+    assert call(a3=P + 8) == _lib.EALIGN
+    assert call(a10=P + 8) == _lib.EALIGN
+    assert call(a11=P + 2) == _lib.EALIGN
+    assert call(a7=1 << 40) == _lib.ERANGE

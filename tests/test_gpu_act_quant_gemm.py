@@ -1,0 +1,86 @@
+"""GPU parity for fp8_act_quant_gemm (act_quant then the block GEMM, one call).
+
+For bf16 activations with m <= 2 the whole computation runs in one kernel
+(quantization in the GEMM's prologue); larger m and fp32 activations queue the
+two kernels.  Every case checks:
+
+* the returned codes and scales are bit-identical to the oracle's act_quant;
+* C is bit-identical to the two-call path (fp8_act_quant, then
+  fp8_block_gemm on its outputs) -- same codes, same scales, same kernel
+  arithmetic;
+* C is within the oracle GEMM's bound (1e-3 * sum |a b|, + 1 bf16 ulp).
+
+Cases: the decode workloads M = 1, 2 (fused) and 3, 4, 8, 64 (two kernels), both
+scale formats, fp32 output, ragged N, a single K block, the long-K decode
+shape (K = 18432), fp32 activations, and the Python binding.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_quant_amd as fb
+import oracle
+from inputs import gen
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x_cpu, w, w_s, scale_fmt, out, label):
+    G.announce(f"act_quant_gemm {label} x={tuple(x_cpu.shape)} {x_cpu.dtype} N={w.shape[0]} fmt={scale_fmt} out={out}")
+    dev = G.device()
+    x = x_cpu.to(dev)
+    got, codes, scales = G.act_quant_gemm(x, w, w_s, scale_fmt, out)
+    wq, ws = oracle.act_quant(x_cpu.float().numpy(), 128, scale_fmt)
+    assert np.array_equal(codes, wq), "codes differ from act_quant"
+    assert np.array_equal(scales.view(np.uint32), ws.view(np.uint32)), "scales differ from act_quant"
+    a2, s2 = G.act_quant(x, scale_fmt)
+    two_call = G.block_gemm(a2, s2, w, w_s, out)
+    assert np.array_equal(got.view(np.uint64), two_call.view(np.uint64)), \
+        f"{int((got != two_call).sum())} outputs differ from the two-call path"
+    c = oracle.fp8_gemm(wq, ws, w, w_s)
+    tol = oracle.gemm_tolerance(wq, ws, w, w_s)
+    ok = oracle.gemm_check(got, c, tol, out)
+    assert ok.all(), f"{int((~ok).sum())} elements out of the oracle bound"
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 64])
+def test_decode_workloads(m):
+    d = gen.decode_gemm(m)
+    _run(d["x"], d["w"], d["w_s"], None, "bf16", "decode")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_ue8m0_and_fp32_out(m):
+    d = gen.custom_gemm(seed=50 + m, m=m, n=2304, k=7168)
+    _run(d["x"], d["w"], d["w_s"], "ue8m0", "f32", "ue8m0/f32")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 129, 128), (4, 17, 256), (2, 7168, 18432), (7, 500, 640)])
+def test_shapes(m, n, k):
+    d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
+    _run(d["x"], d["w"], d["w_s"], None, "bf16", "shape")
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_fp32_activations(m):
+    d = gen.custom_gemm(seed=70 + m, m=m, n=512, k=1024, dtype="f32")
+    _run(d["x"], d["w"], d["w_s"], None, "f32", "fp32 x")
+
+
+def test_python_binding():
+    d = gen.decode_gemm(2)
+    G.announce("act_quant_gemm binding M=2")
+    dev = G.device()
+    x = d["x"].to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    ws = torch.from_numpy(d["w_s"]).to(dev)
+    c, y, s = fb.act_quant_gemm(x, w, ws)
+    y2, s2 = fb.act_quant(x)
+    c2 = fb.fp8_gemm(y2, s2, w, ws)
+    assert c.dtype == torch.bfloat16 and tuple(c.shape) == (2, 18432)
+    assert torch.equal(y.view(torch.uint8), y2.view(torch.uint8)) and torch.equal(s, s2)
+    assert torch.equal(c, c2)
+    with pytest.raises(ValueError):
+        fb.act_quant_gemm(d["x"], w, ws)      # CPU activations: no fallback
