@@ -339,6 +339,10 @@ constexpr int kDecodeWaves = 4, kDecodeMaxM = 64, kDecodeMaxKb = 160;
 // grows with m: at m = 1 the one launch beats act_quant + GEMM by about 5%,
 // at m = 2 they tie, and at m = 4 two launches are faster.
 constexpr int kFusedMaxM = 2;
+// B ring depth of the single-tile (m <= 16) configuration: deep enough to keep
+// the weight stream busy, shallow enough (96 VGPRs) for five waves per SIMD, so
+// every workgroup of an N = 18432 launch is resident at once.
+constexpr int kDecodeDepth1 = 6;
 
 // Fused prologue: quantize x [m, k] bf16 (m <= kFusedMaxM) per 1 x 128 block
 // exactly as the act_quant kernel does -- sixteen lanes per block, 8 elements
@@ -537,7 +541,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
                          a_s, b, b_s, c, m, n, k);                                               \
   } while (0)
     switch ((m + 15) / 16) {
-      case 1: FP8BSQ_DECODE(1, 1, 8); break;
+      case 1: FP8BSQ_DECODE(1, 1, kDecodeDepth1); break;
       case 2: FP8BSQ_DECODE(2, 2, 4); break;
       case 3: FP8BSQ_DECODE(3, 2, 4); break;
       default: FP8BSQ_DECODE(4, 2, 4); break;
@@ -561,10 +565,10 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
   const dim3 grid((unsigned)((n + 15) / 16)), block(64 * kDecodeWaves);
   const size_t lds = (size_t)(m * k);
   if (c_bf16)
-    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, 1, 8, true>), grid, block, lds, stream,
+    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, 1, kDecodeDepth1, true>), grid, block, lds, stream,
                        (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, ue8m0, a_q, a_s);
   else
-    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, 1, 8, true>), grid, block, lds, stream,
+    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, 1, kDecodeDepth1, true>), grid, block, lds, stream,
                        (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, ue8m0, a_q, a_s);
   return hipGetLastError();
 }
