@@ -19,7 +19,10 @@ and, producing the GEMM's weight operand,
 and a linear layer's forward product in one call (act_quant, then fp8_gemm;
 a single kernel for bf16 decode batches of up to 2 rows),
 
-* ``act_quant_gemm(x, b, b_s, scale_fmt=None, out_dtype=torch.bfloat16) -> (c, y, s)``
+* ``act_quant_gemm(x, b, b_s, scale_fmt=None, out_dtype=torch.bfloat16, bias=None) -> (c, y, s)``
+
+``Linear`` (in ``fp8_block_scaled_quant_amd.linear``) wraps the last one as a
+``torch.nn.Module`` holding an E4M3 weight and its 128x128 block scales.
 """
 
 import ctypes
@@ -28,8 +31,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["act_quant", "weight_dequant", "weight_quant", "fp8_gemm", "act_quant_gemm", "Fp8Error",
-           "library_path", "load_library"]
+__all__ = ["act_quant", "weight_dequant", "weight_quant", "fp8_gemm", "act_quant_gemm", "Linear",
+           "Fp8Error", "library_path", "load_library"]
 
 Fp8Error = _lib.Fp8Error
 library_path = _lib.library_path
@@ -170,14 +173,15 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Ten
 
 
 def act_quant_gemm(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, scale_fmt=None,
-                   out_dtype: torch.dtype = torch.bfloat16):
+                   out_dtype: torch.dtype = torch.bfloat16, bias: torch.Tensor = None):
     """``act_quant(x)`` then ``fp8_gemm`` with the weight ``b`` [N, K] / ``b_s``.
 
-    Returns ``(c [..., N], y, s)`` where ``(y, s)`` are act_quant's outputs,
-    bit-identical to calling ``act_quant`` separately.
+    ``bias`` ([N], ``out_dtype``) is added to the FP32 accumulator before the
+    output rounding.  Returns ``(c [..., N], y, s)`` where ``(y, s)`` are
+    act_quant's outputs, bit-identical to calling ``act_quant`` separately.
     """
     b = _codes(b)
-    _require_gpu(x, b, b_s)
+    _require_gpu(x, b, b_s, *(() if bias is None else (bias,)))
     if x.dtype not in _DTYPE:
         raise TypeError("act_quant_gemm takes bf16 or fp32 activations")
     if scale_fmt not in _SCALE_FMT:
@@ -194,6 +198,8 @@ def act_quant_gemm(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, scale_fm
     n = b.shape[0]
     if tuple(b_s.shape) != (-(-n // 128), k // 128):
         raise ValueError("b_s must be [ceil(N/128), K/128]")
+    if bias is not None and (bias.dtype != out_dtype or tuple(bias.shape) != (n,)):
+        raise ValueError(f"bias must be [{n}] of the output dtype {out_dtype}")
     m = x.numel() // k if k else 0
     y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     s = torch.empty(x.shape[:-1] + (k // 128,), dtype=torch.float32, device=x.device)
@@ -202,6 +208,10 @@ def act_quant_gemm(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, scale_fm
         _lib.check(_lib.lib().fp8_act_quant_gemm(
             ctypes.c_void_p(x.data_ptr()), _DTYPE[x.dtype], _SCALE_FMT[scale_fmt],
             ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),
+            ctypes.c_void_p(None if bias is None else bias.data_ptr()),
             ctypes.c_void_p(c.data_ptr()), _DTYPE[out_dtype], m, n, k,
             ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(s.data_ptr()), _stream_handle(x)))
     return c, y.view(torch.float8_e4m3fn), s
+
+
+from .linear import Linear  # noqa: E402  (uses the functions above)

@@ -50,7 +50,7 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.fp8_weight_quant.restype = i32
     lib.fp8_block_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     lib.fp8_block_gemm.restype = i32
-    lib.fp8_act_quant_gemm.argtypes = [vp, i32, i32, vp, vp, vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.fp8_act_quant_gemm.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, vp]
     lib.fp8_act_quant_gemm.restype = i32
     lib.fp8bsq_strerror.argtypes = [i32]
     lib.fp8bsq_strerror.restype = ctypes.c_char_p

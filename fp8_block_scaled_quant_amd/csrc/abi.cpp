@@ -77,8 +77,8 @@ int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const f
 }
 
 int fp8_act_quant_gemm(const void *x, int x_dtype, int scale_fmt, const uint8_t *b,
-                       const float *b_s, void *c, int c_dtype, int64_t m, int64_t n, int64_t k,
-                       uint8_t *a_q, float *a_s, void *hip_stream) {
+                       const float *b_s, const void *bias, void *c, int c_dtype, int64_t m,
+                       int64_t n, int64_t k, uint8_t *a_q, float *a_s, void *hip_stream) {
   if (!x || !b || !b_s || !c || !a_q || !a_s) return FP8BSQ_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return FP8BSQ_EINVAL;
   if (x_dtype != FP8BSQ_F32 && x_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
@@ -86,20 +86,20 @@ int fp8_act_quant_gemm(const void *x, int x_dtype, int scale_fmt, const uint8_t 
   if (scale_fmt != FP8BSQ_SCALE_NONE && scale_fmt != FP8BSQ_SCALE_UE8M0) return FP8BSQ_EINVAL;
   if (k % 128 != 0) return FP8BSQ_ESHAPE;
   if (!aligned(x, 16) || !aligned(b, 16) || !aligned(b_s, 4) || !aligned(c, 4) ||
-      !aligned(a_q, 16) || !aligned(a_s, 4))
+      !aligned(a_q, 16) || !aligned(a_s, 4) || !aligned(bias, c_dtype == FP8BSQ_F32 ? 4 : 2))
     return FP8BSQ_EALIGN;
   if (m > kMaxGemmRows || n >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
   if ((m * (k / 128) + 31) / 32 >= kMaxDim) return FP8BSQ_ERANGE;
   const hipStream_t st = (hipStream_t)hip_stream;
   const bool x_bf16 = x_dtype == FP8BSQ_BF16, ue8m0 = scale_fmt == FP8BSQ_SCALE_UE8M0;
   if (fp8bsq::act_quant_gemm_fusable(x_bf16, m, k))
-    return launch_status(fp8bsq::launch_act_quant_gemm_fused(x, ue8m0, b, b_s, c,
+    return launch_status(fp8bsq::launch_act_quant_gemm_fused(x, ue8m0, b, b_s, bias, c,
                                                             c_dtype == FP8BSQ_BF16, m, n, k, a_q,
                                                             a_s, st));
   const int rc = launch_status(fp8bsq::launch_act_quant(x, x_bf16, m * (k / 128), ue8m0, a_q, a_s, st));
   if (rc != FP8BSQ_OK) return rc;
   return launch_status(fp8bsq::launch_block_gemm(a_q, a_s, b, b_s, c, c_dtype == FP8BSQ_BF16, m, n,
-                                                 k, st));
+                                                 k, st, bias));
 }
 
 const char *fp8bsq_strerror(int status) {

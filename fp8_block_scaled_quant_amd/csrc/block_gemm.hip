@@ -34,6 +34,14 @@ __device__ __forceinline__ i32x8 load_frag(const uint8_t *p) {
                (int)hi.w};
 }
 
+// Optional bias of the output's dtype, added to the FP32 accumulator before
+// the output rounding; `bias` may be null.
+__device__ __forceinline__ float bias_at(const void *bias, bool bf16, int64_t col) {
+  if (!bias) return 0.0f;
+  return bf16 ? __uint_as_float((uint32_t)((const uint16_t *)bias)[col] << 16)
+              : ((const float *)bias)[col];
+}
+
 __device__ __forceinline__ void store_out(void *c, bool bf16, int64_t idx, float v) {
   if (bf16)
     ((uint16_t *)c)[idx] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
@@ -48,7 +56,8 @@ __device__ __forceinline__ void store_out(void *c, bool bf16, int64_t idx, float
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
-    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k) {
+    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
+    const void *__restrict__ bias) {
   const int nkb = (int)(k / kBlock);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t m0 = (int64_t)blockIdx.y * 64 + (wave >> 1) * 32;
@@ -97,10 +106,11 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t col = n0 + 16 * j + lr;
+      const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + 16 * i + lq + r;
-        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][r]);
+        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][r] + bv);
       }
     }
 }
@@ -196,7 +206,7 @@ template <bool kBf16Out>
 __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, const void *__restrict__ bias) {
   __shared__ __attribute__((aligned(1024))) TileSmem sm;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -310,10 +320,11 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t col = n0 + wn + 16 * j + fr;
+      const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = m0 + wm + 16 * i + 4 * fq + e;
-        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][e]);
+        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][e] + bv);
       }
     }
 }
@@ -383,7 +394,8 @@ template <bool kBf16Out, int kMT, int kNT, int kDepth, bool kFuseQ = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
-    bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr, float *__restrict__ a_s_out = nullptr) {
+    const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
+    float *__restrict__ a_s_out = nullptr) {
   constexpr int kRows = 16 * kMT;
   __shared__ float as_t[kDecodeMaxKb][kRows];   // [kb][row], zero-padded rows
   __shared__ f32x4 red[kDecodeWaves - 1][kMT * kNT][64];
@@ -500,12 +512,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const int64_t col = n0 + 16 * nt + fr;
+    const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = 16 * mt + 4 * fq + e;
-        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][nt][e]);
+        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][nt][e] + bv);
       }
   }
 }
@@ -514,7 +527,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
 
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
-                             int64_t k, hipStream_t stream) {
+                             int64_t k, hipStream_t stream, const void *bias) {
   // the tiled kernel addresses A, B and a_s with 32-bit per-lane offsets
   const bool offsets_fit = m * k < ((int64_t)1 << 32) && n * k < ((int64_t)1 << 32);
   if (m > 64 && offsets_fit) {
@@ -522,10 +535,10 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
     if (c_bf16)
       hipLaunchKernelGGL(block_gemm_tile_kernel<true>, grid, block, 0, stream, a, a_s, b, b_s, c, m,
-                         n, k, tiles_m, tiles_n);
+                         n, k, tiles_m, tiles_n, bias);
     else
       hipLaunchKernelGGL(block_gemm_tile_kernel<false>, grid, block, 0, stream, a, a_s, b, b_s, c,
-                         m, n, k, tiles_m, tiles_n);
+                         m, n, k, tiles_m, tiles_n, bias);
     return hipGetLastError();
   }
   if (m <= kDecodeMaxM && k / kBlock <= kDecodeMaxKb) {
@@ -535,10 +548,10 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
     const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)));                                  \
     if (c_bf16)                                                                                  \
       hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, NT, D>), grid, block, 0, stream, a,  \
-                         a_s, b, b_s, c, m, n, k);                                               \
+                         a_s, b, b_s, c, m, n, k, bias);                                         \
     else                                                                                         \
       hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, NT, D>), grid, block, 0, stream, a, \
-                         a_s, b, b_s, c, m, n, k);                                               \
+                         a_s, b, b_s, c, m, n, k, bias);                                         \
   } while (0)
     switch ((m + 15) / 16) {
       case 1: FP8BSQ_DECODE(1, 1, kDecodeDepth1); break;
@@ -552,24 +565,25 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), block(256);
   if (c_bf16)
     hipLaunchKernelGGL(block_gemm_simple_kernel<true>, grid, block, 0, stream, a, a_s, b, b_s, c,
-                       m, n, k);
+                       m, n, k, bias);
   else
     hipLaunchKernelGGL(block_gemm_simple_kernel<false>, grid, block, 0, stream, a, a_s, b, b_s, c,
-                       m, n, k);
+                       m, n, k, bias);
   return hipGetLastError();
 }
 
 hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t *b,
-                                      const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
-                                      int64_t k, uint8_t *a_q, float *a_s, hipStream_t stream) {
+                                      const float *b_s, const void *bias, void *c, bool c_bf16,
+                                      int64_t m, int64_t n, int64_t k, uint8_t *a_q, float *a_s,
+                                      hipStream_t stream) {
   const dim3 grid((unsigned)((n + 15) / 16)), block(64 * kDecodeWaves);
   const size_t lds = (size_t)(m * k);
   if (c_bf16)
     hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, 1, kDecodeDepth1, true>), grid, block, lds, stream,
-                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, ue8m0, a_q, a_s);
+                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
   else
     hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, 1, kDecodeDepth1, true>), grid, block, lds, stream,
-                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, ue8m0, a_q, a_s);
+                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
   return hipGetLastError();
 }
 

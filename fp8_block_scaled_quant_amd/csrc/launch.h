@@ -20,17 +20,18 @@ hipError_t launch_weight_dequant(const uint8_t *x, const float *s, int64_t m, in
 hipError_t launch_weight_quant(const void *x, bool x_bf16, int64_t m, int64_t n, bool ue8m0,
                                uint8_t *y, float *s, hipStream_t stream);
 
-// C[m, n] = block-scaled A[m, k] . B[n, k]^T.
+// C[m, n] = block-scaled A[m, k] . B[n, k]^T (+ bias[n] of C's dtype, if not null).
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
-                             int64_t k, hipStream_t stream);
+                             int64_t k, hipStream_t stream, const void *bias = nullptr);
 
 // Fused act_quant + decode GEMM (bf16 x [m, k], m small enough for
-// act_quant_gemm_fusable): C = Q(x) . B^T; a_q / a_s receive act_quant's codes
-// and scales.
+// act_quant_gemm_fusable): C = Q(x) . B^T (+ bias); a_q / a_s receive
+// act_quant's codes and scales.
 hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t *b,
-                                      const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
-                                      int64_t k, uint8_t *a_q, float *a_s, hipStream_t stream);
+                                      const float *b_s, const void *bias, void *c, bool c_bf16,
+                                      int64_t m, int64_t n, int64_t k, uint8_t *a_q, float *a_s,
+                                      hipStream_t stream);
 bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k);
 
 }  // namespace fp8bsq

@@ -169,8 +169,8 @@ FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t 
  * Per-Block Scaling in DeepSeek-V3 FP8 GEMM", section "Relationship to FP8
  * GEMM Operations", gives the GEMM.  This entry point computes
  *     (a_q, a_s) = fp8_act_quant(x, scale_fmt);
- *     c          = fp8_block_gemm(a_q, a_s, b, b_s)
- * with outputs bit-identical to those two calls.  For bf16 x with m <= 2 (the
+ *     c          = fp8_block_gemm(a_q, a_s, b, b_s)  (+ bias)
+ * with outputs bit-identical to those two calls when bias is null.  For bf16 x with m <= 2 (the
  * decode case) both happen in one kernel: every workgroup quantizes x into
  * LDS in its prologue, and workgroup 0 also writes a_q and a_s.  Otherwise
  * the two kernels are queued back to back on hip_stream.
@@ -180,16 +180,19 @@ FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t 
  *   scale_fmt  as for fp8_act_quant.
  *   b, b_s     [n, k] E4M3 weight (16-byte aligned) and its
  *              [ceil(n / 128), k / 128] FP32 block scales, as for fp8_block_gemm.
+ *   bias       [n] of c's dtype, or NULL; added to the FP32 accumulator
+ *              before the output rounding.
  *   c          [m, n] out, dtype c_dtype (FP8BSQ_F32 or FP8BSQ_BF16).
  *   m, n, k    m, n >= 1; k >= 128 and k % 128 == 0 (else FP8BSQ_ESHAPE).
  *   a_q        [m, k] E4M3 codes out (16-byte aligned): act_quant's y.
  *   a_s        [m, k / 128] FP32 scales out (4-byte aligned): act_quant's s.
  *
- * c meets fp8_block_gemm's bound; a_q and a_s are bit-identical to the oracle.
+ * c meets fp8_block_gemm's bound (around the exact product plus bias); a_q and
+ * a_s are bit-identical to the oracle.
  */
 FP8BSQ_API int fp8_act_quant_gemm(const void *x, int x_dtype, int scale_fmt, const uint8_t *b,
-                       const float *b_s, void *c, int c_dtype, int64_t m, int64_t n, int64_t k,
-                       uint8_t *a_q, float *a_s, void *hip_stream);
+                       const float *b_s, const void *bias, void *c, int c_dtype, int64_t m,
+                       int64_t n, int64_t k, uint8_t *a_q, float *a_s, void *hip_stream);
 
 /* Short English text for a status code; never NULL. */
 FP8BSQ_API const char *fp8bsq_strerror(int status);

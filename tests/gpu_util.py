@@ -133,7 +133,8 @@ def block_gemm(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray, o
     return raw.view(np.float32).reshape(m, n).astype(np.float64)
 
 
-def act_quant_gemm(x: torch.Tensor, b: np.ndarray, b_s: np.ndarray, scale_fmt=None, out: str = "bf16"):
+def act_quant_gemm(x: torch.Tensor, b: np.ndarray, b_s: np.ndarray, scale_fmt=None, out: str = "bf16",
+                   bias: torch.Tensor = None):
     """Fused entry point.  x: CUDA bf16/fp32 [m, k].
 
     Returns (C float64 numpy, codes uint8 numpy, scales fp32 numpy).
@@ -151,6 +152,7 @@ def act_quant_gemm(x: torch.Tensor, b: np.ndarray, b_s: np.ndarray, scale_fmt=No
     fmt = _lib.SCALE_UE8M0 if scale_fmt == "ue8m0" else _lib.SCALE_NONE
     st = _lib.lib().fp8_act_quant_gemm(ctypes.c_void_p(x.data_ptr()), dt, fmt,
                                        ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(bsd.data_ptr()),
+                                       ctypes.c_void_p(None if bias is None else bias.data_ptr()),
                                        ctypes.c_void_p(c.ptr), _lib.BF16 if out == "bf16" else _lib.F32,
                                        m, n, k, ctypes.c_void_p(y.ptr), ctypes.c_void_p(s.ptr), stream())
     assert st == _lib.OK, st

@@ -115,7 +115,7 @@ def test_weight_quant_validation(lib):
 
 def test_act_quant_gemm_validation(lib):
     f = lib.fp8_act_quant_gemm
-    ok = (P, 1, 0, P, P, P, 1, 4, 256, 512, P, P, None)
+    ok = (P, 1, 0, P, P, None, P, 1, 4, 256, 512, P, P, None)
 
     def call(**kw):
         args = list(ok)
@@ -125,15 +125,16 @@ def test_act_quant_gemm_validation(lib):
 
     assert call(a0=None) == _lib.EINVAL
     assert call(a3=None) == _lib.EINVAL
-    assert call(a10=None) == _lib.EINVAL
     assert call(a11=None) == _lib.EINVAL
-    assert call(a7=0) == _lib.EINVAL
+    assert call(a12=None) == _lib.EINVAL
+    assert call(a8=0) == _lib.EINVAL
     assert call(a1=5) == _lib.EINVAL
     assert call(a2=2) == _lib.EINVAL
-    assert call(a6=9) == _lib.EINVAL
-    assert call(a9=200) == _lib.ESHAPE
+    assert call(a7=9) == _lib.EINVAL
+    assert call(a10=200) == _lib.ESHAPE
     assert call(a0=P + 8) == _lib.EALIGN
     assert call(a3=P + 8) == _lib.EALIGN
-    assert call(a10=P + 8) == _lib.EALIGN
-    assert call(a11=P + 2) == _lib.EALIGN
-    assert call(a7=1 << 40) == _lib.ERANGE
+    assert call(a11=P + 8) == _lib.EALIGN
+    assert call(a12=P + 2) == _lib.EALIGN
+    assert call(a5=P + 1) == _lib.EALIGN          # bf16 bias must be 2-byte aligned
+    assert call(a8=1 << 40) == _lib.ERANGE

@@ -84,3 +84,25 @@ def test_python_binding():
     assert torch.equal(c, c2)
     with pytest.raises(ValueError):
         fb.act_quant_gemm(d["x"], w, ws)      # CPU activations: no fallback
+
+
+@pytest.mark.parametrize("m,n,k,out", [
+    (1, 2304, 7168, "bf16"),     # one kernel
+    (2, 300, 1024, "f32"),       # one kernel, ragged N
+    (9, 500, 640, "bf16"),       # decode GEMM after act_quant
+    (100, 384, 512, "f32"),      # tiled GEMM
+    (3, 256, 20608, "bf16"),     # K beyond the decode kernel's range: reference-structure kernel
+])
+def test_bias_in_epilogue(m, n, k, out):
+    d = gen.custom_gemm(seed=m + n + k, m=m, n=n, k=k)
+    G.announce(f"act_quant_gemm bias m={m} n={n} k={k} out={out}")
+    dtype = torch.bfloat16 if out == "bf16" else torch.float32
+    bias = torch.from_numpy(np.random.default_rng(m).standard_normal(n).astype(np.float32) * 4).to(dtype)
+    got, codes, scales = G.act_quant_gemm(d["x"].to(G.device()), d["w"], d["w_s"], None, out,
+                                          bias=bias.to(G.device()))
+    wq, ws = oracle.act_quant(d["x"].float().numpy(), 128, None)
+    assert np.array_equal(codes, wq) and np.array_equal(scales.view(np.uint32), ws.view(np.uint32))
+    c = oracle.fp8_gemm(wq, ws, d["w"], d["w_s"]) + bias.float().double().numpy()[None, :]
+    tol = oracle.gemm_tolerance(wq, ws, d["w"], d["w_s"])
+    ok = oracle.gemm_check(got, c, tol, out)
+    assert ok.all(), f"{int((~ok).sum())} elements out of the bound"
