@@ -10,7 +10,9 @@ Functions follow the call shapes the pages give:
 
 * ``act_quant(x, block_size=128, scale_fmt=None) -> (y, s)``
 * ``weight_dequant(x, s, block_size=128, out_dtype=torch.float32) -> y``
-* ``fp8_gemm(a, a_s, b, b_s, out_dtype=torch.bfloat16) -> c``
+* ``fp8_gemm(a, a_s, b, b_s, out_dtype=torch.bfloat16, scale_fmt=None) -> c``
+  (``scale_fmt="ue8m0"`` declares a_s powers of two: they are then applied
+  inside the MX-scaled MFMA, with a bit-identical result)
 
 and, producing the GEMM's weight operand,
 
@@ -140,12 +142,16 @@ def weight_quant(w: torch.Tensor, block_size: int = 128, scale_fmt=None):
 
 
 def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
-             out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+             out_dtype: torch.dtype = torch.bfloat16, scale_fmt=None) -> torch.Tensor:
     """Block-scaled FP8 GEMM ``C = A . B^T`` (B is the [out, in] weight).
 
     ``a`` [..., K] E4M3 with ``a_s`` [..., K/128]; ``b`` [N, K] E4M3 with
     ``b_s`` [ceil(N/128), K/128].  Returns ``[..., N]`` in ``out_dtype``.
+    ``scale_fmt="ue8m0"`` states that every a_s is a power of two (act_quant's
+    ue8m0 scales) and selects the entry point that applies them in the MFMA.
     """
+    if scale_fmt not in _SCALE_FMT:
+        raise ValueError(f"unknown scale_fmt {scale_fmt!r}")
     a, b = _codes(a), _codes(b)
     _require_gpu(a, a_s, b, b_s)
     if a_s.dtype != torch.float32 or b_s.dtype != torch.float32:
@@ -165,7 +171,8 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Ten
         raise ValueError("b_s must be [ceil(N/128), K/128]")
     c = torch.empty(tuple(a.shape[:-1]) + (n,), dtype=out_dtype, device=a.device)
     if m and n:
-        _lib.check(_lib.lib().fp8_block_gemm(
+        fn = _lib.lib().fp8_block_gemm_ue8m0 if scale_fmt == "ue8m0" else _lib.lib().fp8_block_gemm
+        _lib.check(fn(
             ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(a_s.data_ptr()),
             ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),
             ctypes.c_void_p(c.data_ptr()), _DTYPE[out_dtype], m, n, k, _stream_handle(a)))

@@ -62,8 +62,11 @@ int fp8_weight_quant(const void *x, int x_dtype, int64_t m, int64_t n, int block
                                                    (hipStream_t)hip_stream));
 }
 
-int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
-                   void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
+namespace {
+
+int block_gemm_checked(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
+                       void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream,
+                       bool a_s_pow2) {
   if (!a || !a_s || !b || !b_s || !c) return FP8BSQ_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return FP8BSQ_EINVAL;
   if (c_dtype != FP8BSQ_F32 && c_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
@@ -73,7 +76,19 @@ int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const f
     return FP8BSQ_EALIGN;
   if (m > kMaxGemmRows || n >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
   return launch_status(fp8bsq::launch_block_gemm(a, a_s, b, b_s, c, c_dtype == FP8BSQ_BF16, m, n,
-                                                 k, (hipStream_t)hip_stream));
+                                                 k, (hipStream_t)hip_stream, nullptr, a_s_pow2));
+}
+
+}  // namespace
+
+int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
+                   void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
+  return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream, false);
+}
+
+int fp8_block_gemm_ue8m0(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
+                         void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
+  return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream, true);
 }
 
 int fp8_act_quant_gemm(const void *x, int x_dtype, int scale_fmt, const uint8_t *b,
@@ -99,7 +114,7 @@ int fp8_act_quant_gemm(const void *x, int x_dtype, int scale_fmt, const uint8_t 
   const int rc = launch_status(fp8bsq::launch_act_quant(x, x_bf16, m * (k / 128), ue8m0, a_q, a_s, st));
   if (rc != FP8BSQ_OK) return rc;
   return launch_status(fp8bsq::launch_block_gemm(a_q, a_s, b, b_s, c, c_dtype == FP8BSQ_BF16, m, n,
-                                                 k, st, bias));
+                                                 k, st, bias, ue8m0));
 }
 
 const char *fp8bsq_strerror(int status) {

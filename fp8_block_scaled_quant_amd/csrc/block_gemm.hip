@@ -23,8 +23,17 @@ namespace fp8bsq {
 namespace {
 
 __device__ __forceinline__ f32x4 mfma_e4m3_16x16x128(const i32x8 &a, const i32x8 &b, f32x4 c) {
-  // format 0 = E4M3 for both operands; scale operands unused (plain MFMA).
+  // format 0 = E4M3 for both operands; the literal zero scale operands select
+  // the unscaled instruction (no block scaling inside the matrix core).
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same MFMA with each A row scaled by 2^(e - 127) inside the matrix core:
+// lane l supplies the E8M0 exponent e of the row it feeds (row l % 16); the B
+// scale is 1 (E8M0 127).
+__device__ __forceinline__ f32x4 mfma_e4m3_16x16x128_mx(const i32x8 &a, const i32x8 &b, int e8m0_a) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                          e8m0_a, 0, 127);
 }
 
 __device__ __forceinline__ i32x8 load_frag(const uint8_t *p) {
@@ -202,7 +211,7 @@ __device__ __forceinline__ i32x8 frag_from_lds(const uint8_t *row_base, int fq, 
   return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <bool kBf16Out>
+template <bool kBf16Out, bool kMxA>
 __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
@@ -273,11 +282,22 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       return frag_from_lds(&sm.b[cur][r * kBlock], fq, r);
     };
     i32x8 bcur = read_b(0), bnext;
+    // kMxA (activation scales that are powers of two, act_quant's ue8m0): the
+    // MFMA applies a_s of the A row a lane feeds (its E8M0 exponent, the fp32
+    // exponent field), leaving the rescale a multiply by the wave-uniform b_s.
+    // P * 2^e is exact, so fma(P * a_s, b_s, acc) equals the generic
+    // fma(P, a_s * b_s, acc) bit for bit.
     f32x4 sav[4];
+    int ea[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+    for (int i = 0; i < 4; ++i) {
+      if (kMxA)
+        ea[i] = (int)((__float_as_uint(sm.as[cur][wm + 16 * i + fr]) >> 23) & 0xFFu);
+      else
+        sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+    }
     // MFMA q = 4 j + i; its rescale runs three MFMAs later (ring of 4 partials).
-    // The row scales a_s * b_s are formed at their first use (q - 2 < 4), so
+    // The row scales a_s * b_s are formed at their first use (q - 3 < 4), so
     // their LDS reads never hold up the first MFMAs.
     float sc[4][4];
     f32x4 part[4];
@@ -287,16 +307,17 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = 4 * j + i;
-        part[q % 4] = mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
+        part[q % 4] = kMxA ? mfma_e4m3_16x16x128_mx(af[i], bcur, ea[i])
+                           : mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
         if (q >= 3) {
           const int qp = q - 3, ip = qp % 4, jp = qp / 4;
-          if (qp < 4) {
+          if (!kMxA && qp < 4) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sc[ip][e] = sav[ip][e] * sbv;
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], sc[ip][e], acc[ip][jp][e]);
+            acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       const int ip = qp % 4, jp = qp / 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], sc[ip][e], acc[ip][jp][e]);
+        acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
     }
   };
 
@@ -527,18 +548,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
 
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
-                             int64_t k, hipStream_t stream, const void *bias) {
+                             int64_t k, hipStream_t stream, const void *bias, bool a_s_pow2) {
   // the tiled kernel addresses A, B and a_s with 32-bit per-lane offsets
   const bool offsets_fit = m * k < ((int64_t)1 << 32) && n * k < ((int64_t)1 << 32);
   if (m > 64 && offsets_fit) {
     const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-    if (c_bf16)
-      hipLaunchKernelGGL(block_gemm_tile_kernel<true>, grid, block, 0, stream, a, a_s, b, b_s, c, m,
-                         n, k, tiles_m, tiles_n, bias);
-    else
-      hipLaunchKernelGGL(block_gemm_tile_kernel<false>, grid, block, 0, stream, a, a_s, b, b_s, c,
-                         m, n, k, tiles_m, tiles_n, bias);
+#define FP8BSQ_TILE(BF16, MX)                                                                   \
+  hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX>), grid, block, 0, stream, a, a_s, b, b_s, c, \
+                     m, n, k, tiles_m, tiles_n, bias)
+    if (c_bf16) {
+      if (a_s_pow2) FP8BSQ_TILE(true, true); else FP8BSQ_TILE(true, false);
+    } else {
+      if (a_s_pow2) FP8BSQ_TILE(false, true); else FP8BSQ_TILE(false, false);
+    }
+#undef FP8BSQ_TILE
     return hipGetLastError();
   }
   if (m <= kDecodeMaxM && k / kBlock <= kDecodeMaxKb) {

@@ -21,9 +21,12 @@ hipError_t launch_weight_quant(const void *x, bool x_bf16, int64_t m, int64_t n,
                                uint8_t *y, float *s, hipStream_t stream);
 
 // C[m, n] = block-scaled A[m, k] . B[n, k]^T (+ bias[n] of C's dtype, if not null).
+// a_s_pow2: every a_s is a power of two (act_quant ue8m0), so the tiled kernel
+// may apply it inside the MX-scaled MFMA.
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
-                             int64_t k, hipStream_t stream, const void *bias = nullptr);
+                             int64_t k, hipStream_t stream, const void *bias = nullptr,
+                             bool a_s_pow2 = false);
 
 // Fused act_quant + decode GEMM (bf16 x [m, k], m small enough for
 // act_quant_gemm_fusable): C = Q(x) . B^T (+ bias); a_q / a_s receive

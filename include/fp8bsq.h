@@ -159,6 +159,27 @@ FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t 
                    void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream);
 
 /*
+ * fp8_block_gemm_ue8m0 -- fp8_block_gemm for activation scales that are
+ * powers of two (fp8_act_quant with FP8BSQ_SCALE_UE8M0).
+ *
+ * The page "Understanding Dynamic and Static Activation Quantization Schemes
+ * in DeepSeek-V3", section "How Dynamic Activation Quantization Works", gives
+ * the ue8m0 option: scales rounded to powers of two for hardware
+ * compatibility.  On gfx950 such a scale is an E8M0 number the MX-scaled
+ * matrix instruction applies itself: each A row's a_s is applied inside the
+ * MFMA and the per-K-block rescale multiplies by b_s alone.  Since scaling by
+ * a power of two is exact, the result is bit-identical to fp8_block_gemm on
+ * the same inputs.
+ *
+ * Arguments, layouts and errors as for fp8_block_gemm.  Precondition: every
+ * a_s value is a positive normal power of two; other values give unspecified
+ * (memory-safe) results.
+ */
+FP8BSQ_API int fp8_block_gemm_ue8m0(const uint8_t *a, const float *a_s, const uint8_t *b,
+                         const float *b_s, void *c, int c_dtype, int64_t m, int64_t n, int64_t k,
+                         void *hip_stream);
+
+/*
  * fp8_act_quant_gemm -- a linear layer's forward product in one call:
  * quantize the activations, then multiply by the block-scaled weight.
  *
@@ -173,7 +194,8 @@ FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t 
  * with outputs bit-identical to those two calls when bias is null.  For bf16 x with m <= 2 (the
  * decode case) both happen in one kernel: every workgroup quantizes x into
  * LDS in its prologue, and workgroup 0 also writes a_q and a_s.  Otherwise
- * the two kernels are queued back to back on hip_stream.
+ * the two kernels are queued back to back on hip_stream (with
+ * FP8BSQ_SCALE_UE8M0, the GEMM is fp8_block_gemm_ue8m0's).
  *
  *   x          [m, k] activations, dtype x_dtype (FP8BSQ_F32 or FP8BSQ_BF16),
  *              16-byte aligned.

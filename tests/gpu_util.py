@@ -108,7 +108,7 @@ def weight_dequant(w: np.ndarray, s: np.ndarray, out: str = "bf16", offset: int 
 
 
 def block_gemm(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray, out: str = "bf16",
-               a_dev: torch.Tensor = None, a_s_dev: torch.Tensor = None):
+               a_dev: torch.Tensor = None, a_s_dev: torch.Tensor = None, ue8m0: bool = False):
     """Returns C as float64 numpy (bf16 widened exactly)."""
     dev = device()
     m, k = a.shape if a is not None else a_dev.shape
@@ -119,7 +119,8 @@ def block_gemm(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray, o
     bsd = torch.from_numpy(b_s).to(dev)
     esz = 2 if out == "bf16" else 4
     c = Guarded(m * n * esz)
-    st = _lib.lib().fp8_block_gemm(ctypes.c_void_p(ad.data_ptr()), ctypes.c_void_p(asd.data_ptr()),
+    fn = _lib.lib().fp8_block_gemm_ue8m0 if ue8m0 else _lib.lib().fp8_block_gemm
+    st = fn(ctypes.c_void_p(ad.data_ptr()), ctypes.c_void_p(asd.data_ptr()),
                                    ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(bsd.data_ptr()),
                                    ctypes.c_void_p(c.ptr), _lib.BF16 if out == "bf16" else _lib.F32,
                                    m, n, k, stream())

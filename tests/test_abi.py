@@ -84,8 +84,9 @@ def test_weight_dequant_validation(lib):
     assert f(P, P, 1 << 31, 8, 128, P, 1, None) == _lib.ERANGE
 
 
-def test_block_gemm_validation(lib):
-    f = lib.fp8_block_gemm
+@pytest.mark.parametrize("name", ["fp8_block_gemm", "fp8_block_gemm_ue8m0"])
+def test_block_gemm_validation(lib, name):
+    f = getattr(lib, name)
     assert f(None, P, P, P, P, 1, 16, 16, 128, None) == _lib.EINVAL
     assert f(P, P, P, P, P, 1, 0, 16, 128, None) == _lib.EINVAL
     assert f(P, P, P, P, P, 4, 16, 16, 128, None) == _lib.EINVAL
