@@ -6,8 +6,11 @@ One step = one pass of the whole path over the prefill-shaped linear layer:
      (the act_quant bandwidth workload's shape, 0.1% outliers x100);
   2. weight_dequant of the E4M3 weight [18432, 7168] with its [144, 56]
      block scales to bf16 (the dequant bandwidth workload);
-  3. fp8_block_gemm of the quantized activations with that weight, bf16 out
-     (the prefill GEMM, 8192 x 18432 x 7168).
+  3. the block-scaled GEMM of the quantized activations with that weight,
+     bf16 out (the prefill GEMM, 8192 x 18432 x 7168), through
+     fp8_block_gemm_ue8m0: the activation scales are act_quant's ue8m0 powers
+     of two, applied inside the MX-scaled MFMA (bit-identical to
+     fp8_block_gemm).
 
 ``value`` = 2*M*N*K / step time (TFLOP/s of the whole step, inputs resident
 in HBM).  Per-kernel times come from HIP events recorded on the stream the
@@ -62,7 +65,7 @@ def parse():
     p.add_argument("--profile-workload", default=None,
                    choices=["act_quant", "act_quant_ue8m0", "dequant", "dequant_ragged", "weight_quant",
                             "weight_quant_ue8m0", "decode1", "decode8", "decode32", "decode64",
-                            "prefill1", "prefill2"],
+                            "act_quant_gemm1", "act_quant_gemm2", "prefill1", "prefill2"],
                    help="run only this workload's kernel --iters times (for rocprofv3)")
     p.add_argument("--iters", type=int, default=20)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -100,7 +103,13 @@ def profile_workload(name, iters):
     from inputs import gen
 
     dev = torch.device("cuda:0")
-    if name.startswith("act_quant"):
+    if name.startswith("act_quant_gemm"):
+        d = gen.decode_gemm(int(name[len("act_quant_gemm"):]))
+        x = d["x"].to(dev)
+        w = torch.from_numpy(d["w"]).to(dev)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+        run = lambda: fb.act_quant_gemm(x, w, ws)
+    elif name.startswith("act_quant"):
         x = gen.act_quant_workload()["x"].to(dev)
         fmt = "ue8m0" if name.endswith("ue8m0") else None
         run = lambda: fb.act_quant(x, 128, fmt)
@@ -124,7 +133,7 @@ def profile_workload(name, iters):
         y, s = fb.act_quant(d["x"].to(dev), 128, "ue8m0")
         w = torch.from_numpy(d["w"]).to(dev)
         ws = torch.from_numpy(d["w_s"]).to(dev)
-        run = lambda: fb.fp8_gemm(y, s, w, ws, torch.bfloat16)
+        run = lambda: fb.fp8_gemm(y, s, w, ws, torch.bfloat16, "ue8m0")
     for _ in range(iters):
         run()
     torch.cuda.synchronize()
@@ -209,7 +218,7 @@ def main():
         wd = fb.weight_dequant(w, ws, 128, torch.bfloat16)
         if ev is not None:
             ev[2].record(stream)
-        c = fb.fp8_gemm(y, s, w, ws, torch.bfloat16)
+        c = fb.fp8_gemm(y, s, w, ws, torch.bfloat16, "ue8m0")
         if ev is not None:
             ev[3].record(stream)
         return c, wd
