@@ -430,9 +430,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
     fused_act_quant<kRows>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q, a_s_out,
                            blockIdx.x == 0);
   } else {
-    for (int i = t; i < nkb * kRows; i += 64 * kDecodeWaves) {
-      const int kb = i / kRows, r = i % kRows;
-      as_t[kb][r] = r < m ? a_s[(int64_t)r * nkb + kb] : 0.0f;
+    // a_s [m, nkb] is read in its own (row-major, contiguous) order so the
+    // loads coalesce, eight per thread in flight before any LDS write, and
+    // transposed into as_t; rows m..kRows-1 are zero.
+    const int total = (int)m * nkb;
+    constexpr int kUnroll = 8, kStride = 64 * kDecodeWaves;
+    for (int base = 0; base < total; base += kStride * kUnroll) {
+      float v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + kStride * u + t;
+        v[u] = i < total ? a_s[i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + kStride * u + t;
+        if (i < total) as_t[i % nkb][i / nkb] = v[u];
+      }
+    }
+    for (int i = t; i < nkb * (kRows - (int)m); i += kStride) {
+      const int kb = i / (kRows - (int)m), r = (int)m + i % (kRows - (int)m);
+      as_t[kb][r] = 0.0f;
     }
   }
   __syncthreads();
