@@ -136,13 +136,25 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 // tile whose accumulators still fit in registers moves the fewest bytes per
 // MFMA.
 //
-// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4, and
-// _dword for the 256 activation scales of the K block) into a two-stage ring:
-// K block kb+1 is loaded while kb is computed.  The loads are issued from
-// inline assembly with an explicit vmcnt wait, because the compiler's own
-// handling of LDS DMA waits for every outstanding transfer before any LDS
-// read.  Global addresses are a per-lane 32-bit offset on a wave-uniform
-// 64-bit base, so advancing to the next K block costs scalar adds only.
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4)
+// into a two-stage ring: K block kb+1 is loaded while kb is computed.  The
+// loads are issued from inline assembly with an explicit vmcnt wait, because
+// the compiler's own handling of LDS DMA waits for every outstanding transfer
+// before any LDS read.  Global addresses are a per-lane 32-bit offset on a
+// wave-uniform 64-bit base, so advancing to the next K block costs scalar adds
+// only.
+//
+// Only waves 0-3 issue the DMA, each for itself and for the wave that shares
+// its SIMD (w + 4).  The CU accepts these transfers at about one instruction
+// per 16-18 cycles, so the 64 issued at the top of a K block keep the issuing
+// wave waiting for most of a thousand cycles; with one issuer per SIMD the
+// other wave computes meanwhile instead of queueing behind it.
+//
+// Activation scales: the generic kernel gathers the 256 scales of each K
+// block into LDS (one 4-byte transfer per row).  For power-of-two scales the
+// kernel instead keeps a table of kTabKb K blocks' scales per row, loaded in
+// 16-byte pieces one chunk ahead (double-buffered), which moves the same
+// bytes in an eighth of the transfers.
 //
 // Each wave's 128 columns lie inside one 128-row weight block, so b_s is one
 // scalar per wave and K block.  The per-K-block rescale (4 FMAs per MFMA) is
@@ -162,10 +174,16 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kTileM = 256, kTileN = 256, kThreads = 512;
 
+// K blocks per chunk of the power-of-two scale table
+constexpr int kTabKb = 8;
+
 struct TileSmem {
   uint8_t a[2][kTileM * kBlock];
   uint8_t b[2][kTileN * kBlock];
-  float as[2][kTileM];
+  union {
+    float as[2][kTileM];              // generic: the K block's a_s, per stage
+    float tab[2][kTileM * kTabKb];    // power-of-two a_s: [32-row block][half][row][4 K blocks]
+  };
 };
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -227,19 +245,28 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
   const int64_t grid_n = (n + kBlock - 1) / kBlock;
   const float *bs_row = b_s + min((n0 + wn) / kBlock, grid_n - 1) * nkb;
 
-  // DMA plan: 8-row groups g = wave + 8 i (i < 4) of A and of B; lane p of a
-  // group fills slot p (row 8 g + p / 8, chunk slot p % 8).  Rows past the
-  // matrix edge re-read the last row; their outputs are never stored.
+  // DMA plan: issuing wave d = wave (0..3) covers the 8-row groups
+  // g = d + 4 h + 8 i (h < 2, i < 4) of A and of B; lane p of a group fills
+  // slot p (row 8 g + p / 8, chunk slot p % 8).  Rows past the matrix edge
+  // re-read the last row; their outputs are never stored.
+  const bool dma_wave = wave < 4;
+  const int dw = wave & 3;
   const int dr = lane >> 3, ds = lane & 7;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[8], b_off[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * (wave + 8 * i) + dr;
-    a_off[i] = (uint32_t)(min(m0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
-    b_off[i] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
+  for (int g = 0; g < 8; ++g) {   // g = 4 i + h
+    const int row = 8 * (dw + 4 * (g & 1) + 8 * (g >> 1)) + dr;
+    a_off[g] = (uint32_t)(min(m0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
+    b_off[g] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
   }
-  // scales: wave w, lanes 0..31 -> rows 32 w + lane
-  const uint32_t s_off = (uint32_t)(min(m0 + 32 * wave + (lane & 31), m - 1) * nkb * 4);
+  // scales of the 32-row blocks dw and dw + 4: generic, lanes 0..31 -> rows;
+  // table, lane p -> row p % 32 and K blocks 4 (p / 32) .. +3 of the chunk
+  uint32_t s_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t row = min(m0 + 32 * (dw + 4 * h) + (lane & 31), m - 1);
+    s_off[h] = (uint32_t)(row * nkb * 4 + (kMxA ? (lane >> 5) * 16 : 0));
+  }
   const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]),
                  lds_s = lds_addr(&sm.as[0][0]);
 
@@ -247,11 +274,27 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const uint8_t *ab = a + (int64_t)kb * kBlock;
     const uint8_t *bb = b + (int64_t)kb * kBlock;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lds_dma16(ab, a_off[i], lds_a + s * (kTileM * kBlock) + (wave + 8 * i) * 1024);
-      lds_dma16(bb, b_off[i], lds_b + s * (kTileN * kBlock) + (wave + 8 * i) * 1024);
+    for (int g = 0; g < 8; ++g) {
+      const int grp = dw + 4 * (g & 1) + 8 * (g >> 1);
+      lds_dma16(ab, a_off[g], lds_a + s * (kTileM * kBlock) + grp * 1024);
+      lds_dma16(bb, b_off[g], lds_b + s * (kTileN * kBlock) + grp * 1024);
     }
-    if (lane < 32) lds_dma4(a_s + kb, s_off, lds_s + s * (kTileM * 4) + 32 * wave * 4);
+    if (!kMxA) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (lane < 32) lds_dma4(a_s + kb, s_off[h], lds_s + s * (kTileM * 4) + 32 * (dw + 4 * h) * 4);
+    }
+  };
+  // chunk c of the scale table (K blocks kTabKb c ..), into buffer c & 1; in
+  // a last, half-filled chunk the upper lanes re-read their row's first four
+  // scales (in bounds, never used)
+  auto issue_tab = [&](int c) {
+    const int kb0 = kTabKb * c;
+    const bool inside = kb0 + 4 * (lane >> 5) < nkb;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      lds_dma16(a_s, inside ? s_off[h] + (uint32_t)kb0 * 4 : s_off[h] - (uint32_t)(lane >> 5) * 16,
+                lds_s + (c & 1) * (kTileM * kTabKb * 4) + (dw + 4 * h) * 1024);
   };
 
   const int fr = lane & 15, fq = lane >> 4;
@@ -265,7 +308,11 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const float sbv = bs_row[kb];   // scalar load, issued ahead of the wait below
     wait_dma_all();
     workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
-    if (kb + 1 < nkb) issue(kb + 1, cur ^ 1);
+    if (dma_wave) {
+      if (kb + 1 < nkb) issue(kb + 1, cur ^ 1);
+      // the table buffer of chunk c + 1 was last read in chunk c - 1
+      if (kMxA && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
+    }
     // Retire the scalar load now (the empty asm consumes its value): scalar and
     // LDS results share one counter and the scalar one may return out of order,
     // so while it is outstanding every LDS wait would have to be a full drain.
@@ -289,10 +336,11 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     // fma(P, a_s * b_s, acc) bit for bit.
     f32x4 sav[4];
     int ea[4];
+    const float *tab = &sm.tab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (kMxA)
-        ea[i] = (int)((__float_as_uint(sm.as[cur][wm + 16 * i + fr]) >> 23) & 0xFFu);
+      if (kMxA)   // row wm + 16 i + fr: 32-row block wm / 32 + i / 2, row 16 (i % 2) + fr in it
+        ea[i] = (int)((__float_as_uint(tab[(wm / 32 + i / 2) * 256 + (16 * (i % 2) + fr) * 4]) >> 23) & 0xFFu);
       else
         sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
     }
@@ -332,7 +380,10 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     }
   };
 
-  issue(0, 0);
+  if (dma_wave) {
+    issue(0, 0);
+    if (kMxA) issue_tab(0);
+  }
 #pragma nounroll
   for (int kb = 0; kb < nkb; ++kb) step(kb, kb & 1);
 
@@ -575,10 +626,12 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
 #define FP8BSQ_TILE(BF16, MX)                                                                   \
   hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX>), grid, block, 0, stream, a, a_s, b, b_s, c, \
                      m, n, k, tiles_m, tiles_n, bias)
+    // the power-of-two kernel loads each row's scales in 16-byte pieces
+    const bool mx = a_s_pow2 && (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
     if (c_bf16) {
-      if (a_s_pow2) FP8BSQ_TILE(true, true); else FP8BSQ_TILE(true, false);
+      if (mx) FP8BSQ_TILE(true, true); else FP8BSQ_TILE(true, false);
     } else {
-      if (a_s_pow2) FP8BSQ_TILE(false, true); else FP8BSQ_TILE(false, false);
+      if (mx) FP8BSQ_TILE(false, true); else FP8BSQ_TILE(false, false);
     }
 #undef FP8BSQ_TILE
     return hipGetLastError();
