@@ -150,11 +150,11 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 // wave waiting for most of a thousand cycles; with one issuer per SIMD the
 // other wave computes meanwhile instead of queueing behind it.
 //
-// Activation scales: the generic kernel gathers the 256 scales of each K
-// block into LDS (one 4-byte transfer per row).  For power-of-two scales the
-// kernel instead keeps a table of kTabKb K blocks' scales per row, loaded in
-// 16-byte pieces one chunk ahead (double-buffered), which moves the same
-// bytes in an eighth of the transfers.
+// Activation scales (kTab): the kernel keeps a table of kTabKb K blocks'
+// scales per row, loaded in 16-byte pieces one chunk ahead (double-buffered).
+// Without it (K / 128 not a multiple of 4, or a_s not 16-byte aligned) the 256
+// scales of each K block are gathered one 4-byte transfer per row, eight
+// times the transfers for the same bytes.
 //
 // Each wave's 128 columns lie inside one 128-row weight block, so b_s is one
 // scalar per wave and K block.  The per-K-block rescale (4 FMAs per MFMA) is
@@ -229,7 +229,7 @@ __device__ __forceinline__ i32x8 frag_from_lds(const uint8_t *row_base, int fq, 
   return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <bool kBf16Out, bool kMxA>
+template <bool kBf16Out, bool kMxA, bool kTab>
 __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t row = min(m0 + 32 * (dw + 4 * h) + (lane & 31), m - 1);
-    s_off[h] = (uint32_t)(row * nkb * 4 + (kMxA ? (lane >> 5) * 16 : 0));
+    s_off[h] = (uint32_t)(row * nkb * 4 + (kTab ? (lane >> 5) * 16 : 0));
   }
   const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]),
                  lds_s = lds_addr(&sm.as[0][0]);
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       lds_dma16(ab, a_off[g], lds_a + s * (kTileM * kBlock) + grp * 1024);
       lds_dma16(bb, b_off[g], lds_b + s * (kTileN * kBlock) + grp * 1024);
     }
-    if (!kMxA) {
+    if (!kTab) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         if (lane < 32) lds_dma4(a_s + kb, s_off[h], lds_s + s * (kTileM * 4) + 32 * (dw + 4 * h) * 4);
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     if (dma_wave) {
       if (kb + 1 < nkb) issue(kb + 1, cur ^ 1);
       // the table buffer of chunk c + 1 was last read in chunk c - 1
-      if (kMxA && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
+      if (kTab && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
     }
     // Retire the scalar load now (the empty asm consumes its value): scalar and
     // LDS results share one counter and the scalar one may return out of order,
@@ -337,12 +337,19 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     f32x4 sav[4];
     int ea[4];
     const float *tab = &sm.tab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
+    // table row r = wm + 16 i + x lies in 32-row block wm / 32 + i / 2, at row
+    // 16 (i % 2) + x of it; the MFMA scale wants x = fr, the rescale x = 4 fq + e
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (kMxA)   // row wm + 16 i + fr: 32-row block wm / 32 + i / 2, row 16 (i % 2) + fr in it
-        ea[i] = (int)((__float_as_uint(tab[(wm / 32 + i / 2) * 256 + (16 * (i % 2) + fr) * 4]) >> 23) & 0xFFu);
-      else
+      const float *tb = tab + (wm / 32 + i / 2) * 256 + 16 * (i % 2) * 4;
+      if (kMxA) {
+        ea[i] = (int)((__float_as_uint(tb[fr * 4]) >> 23) & 0xFFu);
+      } else if (kTab) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sav[i][e] = tb[(4 * fq + e) * 4];
+      } else {
         sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+      }
     }
     // MFMA q = 4 j + i; its rescale runs three MFMAs later (ring of 4 partials).
     // The row scales a_s * b_s are formed at their first use (q - 3 < 4), so
@@ -382,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 
   if (dma_wave) {
     issue(0, 0);
-    if (kMxA) issue_tab(0);
+    if (kTab) issue_tab(0);
   }
 #pragma nounroll
   for (int kb = 0; kb < nkb; ++kb) step(kb, kb & 1);
@@ -623,15 +630,20 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   if (m > 64 && offsets_fit) {
     const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-#define FP8BSQ_TILE(BF16, MX)                                                                   \
-  hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX>), grid, block, 0, stream, a, a_s, b, b_s, c, \
+#define FP8BSQ_TILE(BF16, MX, TAB)                                                                   \
+  hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX, TAB>), grid, block, 0, stream, a, a_s, b, b_s, c, \
                      m, n, k, tiles_m, tiles_n, bias)
-    // the power-of-two kernel loads each row's scales in 16-byte pieces
-    const bool mx = a_s_pow2 && (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
+    // the scale table loads each row's scales in 16-byte pieces; the MX-scaled
+    // kernel reads its exponents from it
+    const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
     if (c_bf16) {
-      if (mx) FP8BSQ_TILE(true, true); else FP8BSQ_TILE(true, false);
+      if (tab && a_s_pow2) FP8BSQ_TILE(true, true, true);
+      else if (tab) FP8BSQ_TILE(true, false, true);
+      else FP8BSQ_TILE(true, false, false);
     } else {
-      if (mx) FP8BSQ_TILE(false, true); else FP8BSQ_TILE(false, false);
+      if (tab && a_s_pow2) FP8BSQ_TILE(false, true, true);
+      else if (tab) FP8BSQ_TILE(false, false, true);
+      else FP8BSQ_TILE(false, false, false);
     }
 #undef FP8BSQ_TILE
     return hipGetLastError();

@@ -96,6 +96,27 @@ def test_scale_indexing_probe():
         _assert_close(got, a, a_s, b, b_s, out, label="scale probe")
 
 
+@pytest.mark.parametrize("aligned", [True, False])
+def test_scale_indexing_probe_tiled(aligned):
+    """The tiled kernel with distinct non-power-of-two activation scales per
+    (row, K block): K = 2560 gives two full 8-K-block chunks of the scale table
+    and a half-filled third; a_s offset by one float (not 16-byte aligned)
+    takes the per-K-block gather instead.  Both must meet the bound."""
+    m, n, k = 300, 384, 2560
+    rng = np.random.default_rng(43)
+    a = gen.weight_codes(rng, m, k)
+    b = gen.weight_codes(rng, n, k)
+    a_s = (2.0 ** rng.uniform(-20, 0, (m, k // 128))).astype(np.float32)
+    b_s = (2.0 ** rng.uniform(-20, 0, (n // 128, k // 128))).astype(np.float32)
+    dev = G.device()
+    store = torch.zeros(m * (k // 128) + 1, dtype=torch.float32, device=dev)
+    a_s_dev = (store[:-1] if aligned else store[1:]).view(m, k // 128)
+    a_s_dev.copy_(torch.from_numpy(a_s))
+    G.announce(f"gemm tiled scale-indexing probe, a_s {'aligned' if aligned else 'offset by 4 bytes'}")
+    got = G.block_gemm(None, None, b, b_s, "f32", a_dev=torch.from_numpy(a).to(dev), a_s_dev=a_s_dev)
+    _assert_close(got, a, a_s, b, b_s, "f32", label="tiled scale probe")
+
+
 def test_python_binding_end_to_end():
     from fp8_block_scaled_quant_amd import act_quant, fp8_gemm
     d = gen.custom_gemm(seed=5, m=40, n=256, k=512)
