@@ -409,19 +409,18 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel for M <= 64 (decode).  The weight B [n, k] is streamed from
+// Skinny kernel for M <= 16 (decode).  The weight B [n, k] is streamed from
 // HBM exactly once and dominates the traffic, so the kernel is built to keep
 // many weight bytes in flight with many waves.  A workgroup owns 16 * kNT
 // weight rows; its four waves split the K range four ways (partial sums meet
 // in LDS at the end), and each wave keeps the B fragments of its next kDepth
 // K blocks in registers, issuing the load for block kb + kDepth as it consumes
-// block kb.  A (at most 64 x k codes) is read through the caches as it is
+// block kb.  A (at most 16 x k codes) is read through the caches as it is
 // used: holding its fragments in the ring too was measured slower, because the
-// extra registers halve the waves per SIMD.  kNT = 2 for larger M halves the
-// activation re-reads.  The activation scales are staged once per
-// workgroup in LDS, transposed to [kb][row].  A wave's weight rows lie in one
-// 128-row weight block, so b_s is one scalar per K block.  kMT = ceil(m / 16)
-// MFMA tiles cover the activation rows.
+// extra registers halve the waves per SIMD.  The activation scales are staged
+// once per workgroup in LDS, transposed to [kb][row].  A wave's weight rows
+// lie in one 128-row weight block, so b_s is one scalar per K block.
+// kMT = ceil(m / 16) MFMA tiles cover the activation rows.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4, kDecodeMaxM = 64, kDecodeMaxKb = 160;
 // Activations quantized inside the decode kernel (fused act_quant) for up to
@@ -620,6 +619,161 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel for 16 < M <= 64.  Splitting K across the waves (above) makes
+// every workgroup pull all of A through fragment-shaped loads, twice the
+// weight bytes it streams at M = 64; and since a wave's loads complete in
+// order, each wait for an A fragment also waits for every older weight load in
+// the ring, which shortens the effective prefetch depth to a block or two.
+//
+// Here a workgroup owns 48 weight rows, one 16-row MFMA tile per compute wave
+// (waves 0-2), and all of them walk the same K blocks.  A fourth wave only
+// moves A: it DMAs each K block of A (16 kMT rows x 128 bytes, in whole-line
+// 16-byte pieces, with the XOR swizzle of the tiled kernel) and its kMT x 16
+// activation scales into an LDS ring of kDecode2Slots slots, kDecode2Lead
+// blocks ahead, waiting on its own transfers only.  The compute waves read A
+// fragments and scales from the ring and stream their weight fragments from
+// HBM through a kDepth-deep register ring, so the only vector-memory loads
+// they wait on are their own weight loads.  One barrier per K block hands the
+// ring on.
+// ---------------------------------------------------------------------------
+constexpr int kDecode2Compute = 3;                // compute waves per workgroup (plus the mover)
+constexpr int kDecode2Rows = 16 * kDecode2Compute;   // weight rows per workgroup
+constexpr int kDecode2Lead = 6;                   // K blocks of A in flight ahead of use
+constexpr int kDecode2Slots = kDecode2Lead + 1;   // LDS ring slots
+constexpr int kDecode2Depth = 8;                  // weight ring depth per compute wave
+
+template <int kMT>
+struct Decode2Slot {
+  uint8_t a[16 * kMT * kBlock];   // [row][16-byte chunk slot], swizzled
+  float s[16 * kMT];              // a_s of the K block, per row
+};
+
+// Four waves per workgroup, one per SIMD: with five, two shared a SIMD, and at
+// three waves per SIMD (the kMT = 4 kernel's register count) a second
+// workgroup did not fit on the CU, so part of the grid ran as a second round.
+template <bool kBf16Out, int kMT, int kDepth>
+__global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
+    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
+    const void *__restrict__ bias) {
+  constexpr int kRows = 16 * kMT;
+  constexpr int kDmaPerBlock = kRows / 8 + 1;   // A row groups of 8, then the scales
+  __shared__ __attribute__((aligned(1024))) Decode2Slot<kMT> ring[kDecode2Slots];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool mover = wave == kDecode2Compute;
+  const int nkb = (int)(k / kBlock);
+
+  // mover: lane p of row group g fills chunk slot p % 8 of row 8 g + p / 8;
+  // rows past m re-read row m - 1 and scale lanes past kRows sit idle
+  const int dr = lane >> 3, ds = lane & 7;
+  uint32_t a_off[kRows / 8];
+#pragma unroll
+  for (int g = 0; g < kRows / 8; ++g) {
+    const int row = 8 * g + dr;
+    a_off[g] = (uint32_t)(min((int64_t)row, m - 1) * k + ((ds ^ swz(row)) << 4));
+  }
+  const uint32_t s_off = (uint32_t)(min((int64_t)lane, m - 1) * nkb * 4);
+  const uint32_t lds_ring = lds_addr(&ring[0]);
+  auto issue = [&](int kb) {
+    const uint32_t slot = lds_ring + (uint32_t)((kb % kDecode2Slots) * sizeof(Decode2Slot<kMT>));
+#pragma unroll
+    for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
+    if (lane < kRows) lds_dma4(a_s + kb, s_off, slot + kRows * kBlock);
+  };
+  // wait until K block kb's transfers have landed, given the blocks issued
+  // after it (at most kDecode2Lead - 1 of them)
+  auto wait_block = [&](int behind) {
+    if (behind >= kDecode2Lead - 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDecode2Lead - 1) * kDmaPerBlock) : "memory");
+    else wait_dma_all();
+  };
+
+  const int64_t n0 = (int64_t)blockIdx.x * kDecode2Rows + 16 * (mover ? 0 : wave);
+  const int fr = lane & 15, fq = lane >> 4;
+  const float *bs_row = b_s + min(n0 / kBlock, (n - 1) / kBlock) * nkb;
+  // lane -> (row fr, bytes [16 fq, 16 fq + 16) and [64 + 16 fq, ...)) of a K
+  // block, for the weight from global memory and A from the ring alike
+  const uint8_t *b_src = b + min(n0 + fr, n - 1) * k + 16 * fq;
+  auto load_b = [&](int kb) {
+    const uint8_t *p = b_src + (int64_t)kb * kBlock;
+    const uint4 lo = *(const uint4 *)p, hi = *(const uint4 *)(p + 64);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  const int sw = swz(fr);   // rows 16 mt + fr share their swizzle
+  const uint32_t a_lo = (uint32_t)(fr * kBlock + ((fq ^ sw) << 4));
+  const uint32_t a_hi = (uint32_t)(fr * kBlock + (((4 + fq) ^ sw) << 4));
+
+  // The mover and the compute waves run separate loops with one barrier per K
+  // block plus one after the prologue.  The compute waves' main loop is
+  // branch-free: the compiler's count of weight loads in flight stays exact,
+  // and no ring register is merged across paths (either would make it wait
+  // for every load in flight).
+  if (mover) {
+    for (int kb = 0; kb < kDecode2Lead && kb < nkb; ++kb) issue(kb);
+    wait_block(min(kDecode2Lead, nkb) - 1);
+    workgroup_barrier();
+    for (int kb = 0; kb < nkb; ++kb) {
+      // the slot of kb + lead was last read in block kb - 1
+      if (kb + kDecode2Lead < nkb) issue(kb + kDecode2Lead);
+      if (kb + 1 < nkb) wait_block(min(kb + kDecode2Lead, nkb - 1) - (kb + 1));
+      workgroup_barrier();
+    }
+    return;
+  }
+
+  f32x4 acc[kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const i32x8 &bf, int kb) {
+    const float sb = bs_row[kb];
+    const Decode2Slot<kMT> &sl = ring[kb % kDecode2Slots];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      const uint4 lo = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_lo]);
+      const uint4 hi = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_hi]);
+      const i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const f32x4 sa = *(const f32x4 *)&sl.s[16 * mt + 4 * fq];
+      const f32x4 p = mfma_e4m3_16x16x128(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(p[e], sa[e] * sb, acc[mt][e]);
+    }
+  };
+  // ring slot d holds block kb0 + d; out-of-range refills re-read the last block
+  i32x8 bq[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) bq[d] = load_b(min(d, nkb - 1));
+  workgroup_barrier();
+  const int nfull = nkb / kDepth * kDepth;
+  for (int kb0 = 0; kb0 < nfull; kb0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      compute(bq[d], kb0 + d);
+      // refill after the slot's MFMAs, so the load lands in the slot's own
+      // register rather than in one copied at the loop back-edge
+      __builtin_amdgcn_sched_barrier(0);
+      bq[d] = load_b(min(kb0 + d + kDepth, nkb - 1));
+      workgroup_barrier();
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d)   // the last nkb % kDepth blocks
+    if (nfull + d < nkb) {
+      compute(bq[d], nfull + d);
+      workgroup_barrier();
+    }
+
+  const int64_t col = n0 + fr;
+  const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = 16 * mt + 4 * fq + e;
+      if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][e] + bv);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
@@ -648,7 +802,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
 #undef FP8BSQ_TILE
     return hipGetLastError();
   }
-  if (m <= kDecodeMaxM && k / kBlock <= kDecodeMaxKb) {
+  if (m <= 16 && k / kBlock <= kDecodeMaxKb) {   // K-split decode kernel
     const dim3 block(64 * kDecodeWaves);
 #define FP8BSQ_DECODE(MT, NT, D)                                                                 \
   do {                                                                                           \
@@ -660,13 +814,28 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
       hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, NT, D>), grid, block, 0, stream, a, \
                          a_s, b, b_s, c, m, n, k, bias);                                         \
   } while (0)
-    switch ((m + 15) / 16) {
-      case 1: FP8BSQ_DECODE(1, 1, kDecodeDepth1); break;
-      case 2: FP8BSQ_DECODE(2, 2, 4); break;
-      case 3: FP8BSQ_DECODE(3, 2, 4); break;
-      default: FP8BSQ_DECODE(4, 2, 4); break;
-    }
+    FP8BSQ_DECODE(1, 1, kDecodeDepth1);
 #undef FP8BSQ_DECODE
+    return hipGetLastError();
+  }
+  if (m <= kDecodeMaxM) {
+    const dim3 grid((unsigned)((n + kDecode2Rows - 1) / kDecode2Rows)), block(64 * (kDecode2Compute + 1));
+#define FP8BSQ_DECODE2(MT)                                                                              \
+  do {                                                                                                  \
+    if (c_bf16)                                                                                         \
+      hipLaunchKernelGGL((block_gemm_decode2_kernel<true, MT, kDecode2Depth>), grid, block, 0, stream, a, \
+                         a_s, b, b_s, c, m, n, k, bias);                                                \
+    else                                                                                                \
+      hipLaunchKernelGGL((block_gemm_decode2_kernel<false, MT, kDecode2Depth>), grid, block, 0, stream,  \
+                         a, a_s, b, b_s, c, m, n, k, bias);                                             \
+  } while (0)
+    switch ((m + 15) / 16) {
+      case 1: FP8BSQ_DECODE2(1); break;   // m <= 16 with K beyond the K-split kernel's scale staging
+      case 2: FP8BSQ_DECODE2(2); break;
+      case 3: FP8BSQ_DECODE2(3); break;
+      default: FP8BSQ_DECODE2(4); break;
+    }
+#undef FP8BSQ_DECODE2
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), block(256);

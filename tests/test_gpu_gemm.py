@@ -71,7 +71,8 @@ def test_prefill_workloads_sampled_rows(shape):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (17, 200, 256), (33, 130, 384), (64, 129, 128),
-                                   (100, 300, 1024), (130, 64, 640), (257, 385, 512)])
+                                   (100, 300, 1024), (130, 64, 640), (257, 385, 512),
+                                   (40, 100, 21504), (5, 70, 20608)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_ragged_shapes(m, n, k, out):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
