@@ -409,13 +409,14 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel for M <= 16 (decode).  The weight B [n, k] is streamed from
+// Skinny kernel for M <= 2 (decode), with or without the fused act_quant.
+// The weight B [n, k] is streamed from
 // HBM exactly once and dominates the traffic, so the kernel is built to keep
 // many weight bytes in flight with many waves.  A workgroup owns 16 * kNT
 // weight rows; its four waves split the K range four ways (partial sums meet
 // in LDS at the end), and each wave keeps the B fragments of its next kDepth
 // K blocks in registers, issuing the load for block kb + kDepth as it consumes
-// block kb.  A (at most 16 x k codes) is read through the caches as it is
+// block kb.  A (at most 2 x k codes) is read through the caches as it is
 // used: holding its fragments in the ring too was measured slower, because the
 // extra registers halve the waves per SIMD.  The activation scales are staged
 // once per workgroup in LDS, transposed to [kb][row].  A wave's weight rows
@@ -620,9 +621,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel for 16 < M <= 64.  Splitting K across the waves (above) makes
-// every workgroup pull all of A through fragment-shaped loads, twice the
-// weight bytes it streams at M = 64; and since a wave's loads complete in
+// Decode kernel for 2 < M <= 64 (and smaller M when K is too long for the
+// kernel above).  Splitting K across the waves (above) makes every workgroup pull all
+// of A through fragment-shaped loads, twice the weight bytes it streams at
+// M = 64; and since a wave's loads complete in
 // order, each wait for an A fragment also waits for every older weight load in
 // the ring, which shortens the effective prefetch depth to a block or two.
 //
@@ -641,7 +643,7 @@ constexpr int kDecode2Compute = 3;                // compute waves per workgroup
 constexpr int kDecode2Rows = 16 * kDecode2Compute;   // weight rows per workgroup
 constexpr int kDecode2Lead = 6;                   // K blocks of A in flight ahead of use
 constexpr int kDecode2Slots = kDecode2Lead + 1;   // LDS ring slots
-constexpr int kDecode2Depth = 8;                  // weight ring depth per compute wave
+constexpr int kDecode2Depth = 5;                  // weight ring depth per compute wave
 
 template <int kMT>
 struct Decode2Slot {
@@ -802,7 +804,9 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
 #undef FP8BSQ_TILE
     return hipGetLastError();
   }
-  if (m <= 16 && k / kBlock <= kDecodeMaxKb) {   // K-split decode kernel
+  // K-split decode kernel up to the fused path's M, so that fp8_act_quant_gemm's
+  // one-kernel and two-call paths share their GEMM arithmetic
+  if (m <= kFusedMaxM && k / kBlock <= kDecodeMaxKb) {
     const dim3 block(64 * kDecodeWaves);
 #define FP8BSQ_DECODE(MT, NT, D)                                                                 \
   do {                                                                                           \
@@ -830,7 +834,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
                          a, a_s, b, b_s, c, m, n, k, bias);                                             \
   } while (0)
     switch ((m + 15) / 16) {
-      case 1: FP8BSQ_DECODE2(1); break;   // m <= 16 with K beyond the K-split kernel's scale staging
+      case 1: FP8BSQ_DECODE2(1); break;
       case 2: FP8BSQ_DECODE2(2); break;
       case 3: FP8BSQ_DECODE2(3); break;
       default: FP8BSQ_DECODE2(4); break;
