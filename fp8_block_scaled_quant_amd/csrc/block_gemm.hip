@@ -628,8 +628,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
 // order, each wait for an A fragment also waits for every older weight load in
 // the ring, which shortens the effective prefetch depth to a block or two.
 //
-// Here a workgroup owns 48 weight rows, one 16-row MFMA tile per compute wave
-// (waves 0-2), and all of them walk the same K blocks.  A fourth wave only
+// Here a workgroup owns 80 weight rows, one 16-row MFMA tile per compute wave
+// (waves 0-4), and all of them walk the same K blocks.  A sixth wave only
 // moves A: it DMAs each K block of A (16 kMT rows x 128 bytes, in whole-line
 // 16-byte pieces, with the XOR swizzle of the tiled kernel) and its kMT x 16
 // activation scales into an LDS ring of kDecode2Slots slots, kDecode2Lead
@@ -639,11 +639,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
 // they wait on are their own weight loads.  One barrier per K block hands the
 // ring on.
 // ---------------------------------------------------------------------------
-constexpr int kDecode2Compute = 3;                // compute waves per workgroup (plus the mover)
+constexpr int kDecode2Compute = 5;                // compute waves per workgroup (plus the mover)
 constexpr int kDecode2Rows = 16 * kDecode2Compute;   // weight rows per workgroup
 constexpr int kDecode2Lead = 6;                   // K blocks of A in flight ahead of use
 constexpr int kDecode2Slots = kDecode2Lead + 1;   // LDS ring slots
-constexpr int kDecode2Depth = 5;                  // weight ring depth per compute wave
+constexpr int kDecode2Depth = 6;                  // weight ring depth per compute wave (even)
 
 template <int kMT>
 struct Decode2Slot {
@@ -651,9 +651,13 @@ struct Decode2Slot {
   float s[16 * kMT];              // a_s of the K block, per row
 };
 
-// Four waves per workgroup, one per SIMD: with five, two shared a SIMD, and at
-// three waves per SIMD (the kMT = 4 kernel's register count) a second
-// workgroup did not fit on the CU, so part of the grid ran as a second round.
+// Workgroup size: each workgroup fetches its K blocks of A and their scales
+// once, and the CU's vector-memory issue rate (not HBM) bounded the kernel,
+// so the wider the workgroup the fewer fetches per weight row.  Five compute
+// waves give 231 workgroups for N = 18432, one per CU; three gave 384, two on
+// half the CUs, whose mover then sat ~1000 cycles per K block in DMA issue
+// (M = 64 with weights streaming from HBM: 50.7 us at three, 38.5 at five,
+// 40.7 at six).
 template <bool kBf16Out, int kMT, int kDepth>
 __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
@@ -684,11 +688,18 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
     for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
     if (lane < kRows) lds_dma4(a_s + kb, s_off, slot + kRows * kBlock);
   };
-  // wait until K block kb's transfers have landed, given the blocks issued
-  // after it (at most kDecode2Lead - 1 of them)
+  // wait until a K block's transfers have landed, given how many blocks were
+  // issued after it (transfers complete in issue order)
+  static_assert(kDecode2Lead == 6 && 5 * kDmaPerBlock < 64, "one vmcnt case per block behind");
   auto wait_block = [&](int behind) {
-    if (behind >= kDecode2Lead - 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDecode2Lead - 1) * kDmaPerBlock) : "memory");
-    else wait_dma_all();
+    switch (behind) {
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * kDmaPerBlock) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerBlock) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kDmaPerBlock) : "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kDmaPerBlock) : "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * kDmaPerBlock) : "memory"); break;
+      default: wait_dma_all(); break;
+    }
   };
 
   const int64_t n0 = (int64_t)blockIdx.x * kDecode2Rows + 16 * (mover ? 0 : wave);
@@ -712,13 +723,15 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
   // and no ring register is merged across paths (either would make it wait
   // for every load in flight).
   if (mover) {
+    // the compute waves read block kb + 1 while they compute kb, so by the
+    // barrier that ends block kb, block kb + 2 must have landed
     for (int kb = 0; kb < kDecode2Lead && kb < nkb; ++kb) issue(kb);
-    wait_block(min(kDecode2Lead, nkb) - 1);
+    wait_block(min(kDecode2Lead, nkb) - 1 - min(1, nkb - 1));
     workgroup_barrier();
     for (int kb = 0; kb < nkb; ++kb) {
-      // the slot of kb + lead was last read in block kb - 1
+      // the slot of kb + lead was last read during block kb - 2
       if (kb + kDecode2Lead < nkb) issue(kb + kDecode2Lead);
-      if (kb + 1 < nkb) wait_block(min(kb + kDecode2Lead, nkb - 1) - (kb + 1));
+      if (kb + 2 < nkb) wait_block(min(kb + kDecode2Lead, nkb - 1) - (kb + 2));
       workgroup_barrier();
     }
     return;
@@ -727,30 +740,44 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
   f32x4 acc[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const i32x8 &bf, int kb) {
-    const float sb = bs_row[kb];
+  // A fragments, row scales and b_s of one K block, double-buffered: block
+  // kb + 1's are read from the ring while block kb's feed the MFMAs
+  i32x8 af[2][kMT];
+  f32x4 sa[2][kMT];
+  float sb[2];
+  auto read_a = [&](int kb, int buf) {   // kb may be nkb (a stale slot, never used)
     const Decode2Slot<kMT> &sl = ring[kb % kDecode2Slots];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
       const uint4 lo = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_lo]);
       const uint4 hi = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_hi]);
-      const i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const f32x4 sa = *(const f32x4 *)&sl.s[16 * mt + 4 * fq];
-      const f32x4 p = mfma_e4m3_16x16x128(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+      af[buf][mt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      sa[buf][mt] = *(const f32x4 *)&sl.s[16 * mt + 4 * fq];
+    }
+    sb[buf] = bs_row[min(kb, nkb - 1)];
+  };
+  auto compute = [&](const i32x8 &bf, int buf) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(p[e], sa[e] * sb, acc[mt][e]);
+    for (int mt = 0; mt < kMT; ++mt) {
+      const f32x4 p = mfma_e4m3_16x16x128(af[buf][mt], bf, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(p[e], sa[buf][mt][e] * sb[buf], acc[mt][e]);
     }
   };
-  // ring slot d holds block kb0 + d; out-of-range refills re-read the last block
+  // weight ring slot d holds block kb0 + d; out-of-range refills re-read the
+  // last block.  kDepth is even, so block kb's A buffer is kb & 1 = d & 1.
+  static_assert(kDepth % 2 == 0, "the A double buffer follows the ring slot's parity");
   i32x8 bq[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) bq[d] = load_b(min(d, nkb - 1));
   workgroup_barrier();
+  read_a(0, 0);
   const int nfull = nkb / kDepth * kDepth;
   for (int kb0 = 0; kb0 < nfull; kb0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      compute(bq[d], kb0 + d);
+      read_a(kb0 + d + 1, (d + 1) & 1);
+      compute(bq[d], d & 1);
       // refill after the slot's MFMAs, so the load lands in the slot's own
       // register rather than in one copied at the loop back-edge
       __builtin_amdgcn_sched_barrier(0);
@@ -761,7 +788,8 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d)   // the last nkb % kDepth blocks
     if (nfull + d < nkb) {
-      compute(bq[d], nfull + d);
+      read_a(nfull + d + 1, (d + 1) & 1);
+      compute(bq[d], d & 1);
       workgroup_barrier();
     }
 
