@@ -658,14 +658,22 @@ struct Decode2Slot {
 // half the CUs, whose mover then sat ~1000 cycles per K block in DMA issue
 // (M = 64 with weights streaming from HBM: 50.7 us at three, 38.5 at five,
 // 40.7 at six).
-template <bool kBf16Out, int kMT, int kDepth>
+//
+// Activation scales (kTab): as in the tiled kernel, a double-buffered table of
+// kTabKb K blocks' scales per row, loaded one chunk ahead in 16-byte pieces;
+// otherwise each K block's kRows scales travel in its ring slot, one 4-byte
+// transfer per row.
+template <bool kBf16Out, int kMT, int kDepth, bool kTab>
 __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias) {
   constexpr int kRows = 16 * kMT;
-  constexpr int kDmaPerBlock = kRows / 8 + 1;   // A row groups of 8, then the scales
+  constexpr int kDmaPerBlock = kRows / 8 + (kTab ? 0 : 1);   // A row groups of 8 (+ the scales)
+  // table: [32-row block][half][row][4 K blocks], as the DMA lanes lay it down
+  constexpr int kTabRows = (kRows + 31) / 32 * 32;   // whole 32-row blocks (one DMA each)
   __shared__ __attribute__((aligned(1024))) Decode2Slot<kMT> ring[kDecode2Slots];
+  __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool mover = wave == kDecode2Compute;
@@ -686,7 +694,24 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
     const uint32_t slot = lds_ring + (uint32_t)((kb % kDecode2Slots) * sizeof(Decode2Slot<kMT>));
 #pragma unroll
     for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
-    if (lane < kRows) lds_dma4(a_s + kb, s_off, slot + kRows * kBlock);
+    if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + kRows * kBlock);
+  };
+  // table chunk c into buffer c & 1: instruction i, lane p -> row 32 i + p % 32
+  // and K blocks 4 (p / 32) .. +3 of the chunk; in a half-filled last chunk the
+  // upper half re-reads the row's first four scales (in bounds, never used)
+  const int trow = lane & 31, thalf = lane >> 5;
+  uint32_t t_off[kTabRows / 32];
+#pragma unroll
+  for (int i = 0; i < kTabRows / 32; ++i)
+    t_off[i] = (uint32_t)(min((int64_t)(32 * i + trow), m - 1) * nkb * 4);
+  const uint32_t lds_tab = lds_addr(&stab[0][0]);
+  auto issue_tab = [&](int ch) {
+    const int kb0 = kTabKb * ch;
+    const uint32_t piece = kb0 + 4 * thalf < nkb ? (uint32_t)(kb0 + 4 * thalf) * 4 : 0u;
+#pragma unroll
+    for (int i = 0; i < kTabRows / 32; ++i)
+      if (32 * i + trow < kRows)
+        lds_dma16(a_s, t_off[i] + piece, lds_tab + (ch & 1) * (kTabRows * kTabKb * 4) + i * 1024);
   };
   // wait until a K block's transfers have landed, given how many blocks were
   // issued after it (transfers complete in issue order)
@@ -725,12 +750,17 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
   if (mover) {
     // the compute waves read block kb + 1 while they compute kb, so by the
     // barrier that ends block kb, block kb + 2 must have landed
+    if (kTab) issue_tab(0);
     for (int kb = 0; kb < kDecode2Lead && kb < nkb; ++kb) issue(kb);
     wait_block(min(kDecode2Lead, nkb) - 1 - min(1, nkb - 1));
     workgroup_barrier();
     for (int kb = 0; kb < nkb; ++kb) {
       // the slot of kb + lead was last read during block kb - 2
       if (kb + kDecode2Lead < nkb) issue(kb + kDecode2Lead);
+      // chunk c + 1 into the buffer chunk c - 1 used (last read during block
+      // kb - 2); it is older than block kb + 7's transfers, which are waited
+      // for (two blocks ahead of their use) before its first read
+      if (kTab && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
       if (kb + 2 < nkb) wait_block(min(kb + kDecode2Lead, nkb - 1) - (kb + 2));
       workgroup_barrier();
     }
@@ -752,7 +782,16 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
       const uint4 lo = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_lo]);
       const uint4 hi = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_hi]);
       af[buf][mt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sa[buf][mt] = *(const f32x4 *)&sl.s[16 * mt + 4 * fq];
+      if (kTab) {
+        const float *tb = &stab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * mt + 4 * fq + e;
+          sa[buf][mt][e] = tb[(r >> 5) * 256 + (r & 31) * 4];
+        }
+      } else {
+        sa[buf][mt] = *(const f32x4 *)&sl.s[16 * mt + 4 * fq];
+      }
     }
     sb[buf] = bs_row[min(kb, nkb - 1)];
   };
@@ -852,14 +891,19 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   }
   if (m <= kDecodeMaxM) {
     const dim3 grid((unsigned)((n + kDecode2Rows - 1) / kDecode2Rows)), block(64 * (kDecode2Compute + 1));
-#define FP8BSQ_DECODE2(MT)                                                                              \
-  do {                                                                                                  \
-    if (c_bf16)                                                                                         \
-      hipLaunchKernelGGL((block_gemm_decode2_kernel<true, MT, kDecode2Depth>), grid, block, 0, stream, a, \
-                         a_s, b, b_s, c, m, n, k, bias);                                                \
-    else                                                                                                \
-      hipLaunchKernelGGL((block_gemm_decode2_kernel<false, MT, kDecode2Depth>), grid, block, 0, stream,  \
-                         a, a_s, b, b_s, c, m, n, k, bias);                                             \
+    const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
+#define FP8BSQ_DECODE2_T(MT, TAB)                                                                          \
+  do {                                                                                                     \
+    if (c_bf16)                                                                                            \
+      hipLaunchKernelGGL((block_gemm_decode2_kernel<true, MT, kDecode2Depth, TAB>), grid, block, 0, stream, \
+                         a, a_s, b, b_s, c, m, n, k, bias);                                                \
+    else                                                                                                   \
+      hipLaunchKernelGGL((block_gemm_decode2_kernel<false, MT, kDecode2Depth, TAB>), grid, block, 0,        \
+                         stream, a, a_s, b, b_s, c, m, n, k, bias);                                        \
+  } while (0)
+#define FP8BSQ_DECODE2(MT)                                                                                 \
+  do {                                                                                                     \
+    if (tab) FP8BSQ_DECODE2_T(MT, true); else FP8BSQ_DECODE2_T(MT, false);                                 \
   } while (0)
     switch ((m + 15) / 16) {
       case 1: FP8BSQ_DECODE2(1); break;
@@ -868,6 +912,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
       default: FP8BSQ_DECODE2(4); break;
     }
 #undef FP8BSQ_DECODE2
+#undef FP8BSQ_DECODE2_T
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), block(256);

@@ -72,7 +72,7 @@ def test_prefill_workloads_sampled_rows(shape):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (17, 200, 256), (33, 130, 384), (64, 129, 128),
                                    (100, 300, 1024), (130, 64, 640), (257, 385, 512),
-                                   (40, 100, 21504), (5, 70, 20608)])
+                                   (40, 100, 21504), (5, 70, 20608), (20, 300, 1536)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_ragged_shapes(m, n, k, out):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
@@ -97,13 +97,15 @@ def test_scale_indexing_probe():
         _assert_close(got, a, a_s, b, b_s, out, label="scale probe")
 
 
+@pytest.mark.parametrize("m", [300, 40])
 @pytest.mark.parametrize("aligned", [True, False])
-def test_scale_indexing_probe_tiled(aligned):
-    """The tiled kernel with distinct non-power-of-two activation scales per
-    (row, K block): K = 2560 gives two full 8-K-block chunks of the scale table
-    and a half-filled third; a_s offset by one float (not 16-byte aligned)
-    takes the per-K-block gather instead.  Both must meet the bound."""
-    m, n, k = 300, 384, 2560
+def test_scale_indexing_probe_tiled(m, aligned):
+    """The tiled (M = 300) and staged-activation decode (M = 40) kernels with
+    distinct non-power-of-two activation scales per (row, K block): K = 2560
+    gives two full 8-K-block chunks of the scale table and a half-filled
+    third; a_s offset by one float (not 16-byte aligned) takes the per-K-block
+    scale transfers instead.  Both must meet the bound."""
+    n, k = 384, 2560
     rng = np.random.default_rng(43)
     a = gen.weight_codes(rng, m, k)
     b = gen.weight_codes(rng, n, k)
@@ -113,7 +115,7 @@ def test_scale_indexing_probe_tiled(aligned):
     store = torch.zeros(m * (k // 128) + 1, dtype=torch.float32, device=dev)
     a_s_dev = (store[:-1] if aligned else store[1:]).view(m, k // 128)
     a_s_dev.copy_(torch.from_numpy(a_s))
-    G.announce(f"gemm tiled scale-indexing probe, a_s {'aligned' if aligned else 'offset by 4 bytes'}")
+    G.announce(f"gemm scale-indexing probe m={m}, a_s {'aligned' if aligned else 'offset by 4 bytes'}")
     got = G.block_gemm(None, None, b, b_s, "f32", a_dev=torch.from_numpy(a).to(dev), a_s_dev=a_s_dev)
     _assert_close(got, a, a_s, b, b_s, "f32", label="tiled scale probe")
 
