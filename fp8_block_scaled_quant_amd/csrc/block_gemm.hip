@@ -674,6 +674,13 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
   constexpr int kTabRows = (kRows + 31) / 32 * 32;   // whole 32-row blocks (one DMA each)
   __shared__ __attribute__((aligned(1024))) Decode2Slot<kMT> ring[kDecode2Slots];
   __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
+  // weight path: up to 32 activation rows each compute wave DMAs its weight
+  // rows into an LDS ring (whole-line transfers, half the vector-memory issue
+  // of fragment-shaped loads); above that the waves' A-fragment reads already
+  // load the LDS heavily, and the weight fragments stream into registers
+  constexpr bool kBLds = kMT <= 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t bring[kBLds ? kDecode2Compute : 1][kBLds ? kDepth : 1]
+                                                         [kBLds ? 16 * kBlock : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool mover = wave == kDecode2Compute;
@@ -730,8 +737,26 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
   const int64_t n0 = (int64_t)blockIdx.x * kDecode2Rows + 16 * (mover ? 0 : wave);
   const int fr = lane & 15, fq = lane >> 4;
   const float *bs_row = b_s + min(n0 / kBlock, (n - 1) / kBlock) * nkb;
-  // lane -> (row fr, bytes [16 fq, 16 fq + 16) and [64 + 16 fq, ...)) of a K
-  // block, for the weight from global memory and A from the ring alike
+  // kBLds: each compute wave DMAs its own 16 weight rows of a K block (two
+  // whole-line transfers, same lane plan and swizzle as A) into its own
+  // kDepth-slot LDS ring; no other wave reads them, so they need no barrier.
+  // Addresses are 32-bit lane offsets from the wave's first (clamped) row.
+  const int64_t nb0 = min(n0, n - 1);
+  const uint8_t *b_wave = b + nb0 * k;
+  uint32_t b_off[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int row = 8 * g + dr;
+    b_off[g] = (uint32_t)((min(n0 + row, n - 1) - nb0) * k + ((ds ^ swz(row)) << 4));
+  }
+  const uint32_t lds_b = lds_addr(&bring[kBLds && !mover ? wave : 0][0][0]);
+  auto issue_b = [&](int kb) {
+    const uint32_t slot = lds_b + (uint32_t)((kb % kDepth) * 16 * kBlock);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) lds_dma16(b_wave + (int64_t)kb * kBlock, b_off[g], slot + g * 1024);
+  };
+  // otherwise lane -> (row fr, bytes [16 fq, 16 fq + 16) and [64 + 16 fq, ...))
+  // of a K block straight from global memory, the same bytes A's fragments take
   const uint8_t *b_src = b + min(n0 + fr, n - 1) * k + 16 * fq;
   auto load_b = [&](int kb) {
     const uint8_t *p = b_src + (int64_t)kb * kBlock;
@@ -764,6 +789,7 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
       if (kb + 2 < nkb) wait_block(min(kb + kDecode2Lead, nkb - 1) - (kb + 2));
       workgroup_barrier();
     }
+    wait_dma_all();
     return;
   }
 
@@ -803,34 +829,71 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
       for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(p[e], sa[buf][mt][e] * sb[buf], acc[mt][e]);
     }
   };
-  // weight ring slot d holds block kb0 + d; out-of-range refills re-read the
-  // last block.  kDepth is even, so block kb's A buffer is kb & 1 = d & 1.
-  static_assert(kDepth % 2 == 0, "the A double buffer follows the ring slot's parity");
-  i32x8 bq[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) bq[d] = load_b(min(d, nkb - 1));
-  workgroup_barrier();
-  read_a(0, 0);
-  const int nfull = nkb / kDepth * kDepth;
-  for (int kb0 = 0; kb0 < nfull; kb0 += kDepth) {
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      read_a(kb0 + d + 1, (d + 1) & 1);
-      compute(bq[d], d & 1);
-      // refill after the slot's MFMAs, so the load lands in the slot's own
-      // register rather than in one copied at the loop back-edge
-      __builtin_amdgcn_sched_barrier(0);
-      bq[d] = load_b(min(kb0 + d + kDepth, nkb - 1));
+  if constexpr (kBLds) {
+    i32x8 bf[2];
+    auto read_b = [&](int kb, int buf) {   // kb may be nkb (a stale slot, never used)
+      const uint8_t *sl = &bring[wave][kb % kDepth][0];
+      const uint4 lo = *(const uint4 *)(sl + a_lo), hi = *(const uint4 *)(sl + a_hi);
+      bf[buf] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    // one K block: block kb + 1's weight transfers (issued kDepth - 1 blocks
+    // ago) have landed once at most kDepth - 2 younger blocks' remain; read
+    // its fragments and A's while block kb's feed the MFMAs, then refill the
+    // slot block kb came from (its fragments were read a block ago) with
+    // block kb + kDepth, clamped so that every block issues the same two
+    // transfers
+    static_assert(2 * (kDepth - 1) < 64, "vmcnt range");
+    auto step = [&](int kb, int cur) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kDepth - 2)) : "memory");
+      read_a(kb + 1, cur ^ 1);
+      read_b(kb + 1, cur ^ 1);
+      compute(bf[cur], cur);
+      issue_b(min(kb + kDepth, nkb - 1));
       workgroup_barrier();
+    };
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) issue_b(min(d, nkb - 1));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kDepth - 1)) : "memory");
+    workgroup_barrier();
+    read_a(0, 0);
+    read_b(0, 0);
+    const int neven = nkb & ~1;
+    for (int kb = 0; kb < neven; kb += 2) {
+      step(kb, 0);
+      step(kb + 1, 1);
     }
+    if (nkb & 1) step(neven, 0);
+    wait_dma_all();   // the clamped refills past the last block, before the workgroup's LDS is released
+  } else {
+    // weight ring slot d holds block kb0 + d; out-of-range refills re-read
+    // the last block.  kDepth is even, so block kb's A buffer is kb & 1 = d & 1.
+    static_assert(kDepth % 2 == 0, "the A double buffer follows the ring slot's parity");
+    i32x8 bq[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) bq[d] = load_b(min(d, nkb - 1));
+    workgroup_barrier();
+    read_a(0, 0);
+    const int nfull = nkb / kDepth * kDepth;
+    for (int kb0 = 0; kb0 < nfull; kb0 += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        read_a(kb0 + d + 1, (d + 1) & 1);
+        compute(bq[d], d & 1);
+        // refill after the slot's MFMAs, so the load lands in the slot's own
+        // register rather than in one copied at the loop back-edge
+        __builtin_amdgcn_sched_barrier(0);
+        bq[d] = load_b(min(kb0 + d + kDepth, nkb - 1));
+        workgroup_barrier();
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)   // the last nkb % kDepth blocks
+      if (nfull + d < nkb) {
+        read_a(nfull + d + 1, (d + 1) & 1);
+        compute(bq[d], d & 1);
+        workgroup_barrier();
+      }
   }
-#pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d)   // the last nkb % kDepth blocks
-    if (nfull + d < nkb) {
-      read_a(nfull + d + 1, (d + 1) & 1);
-      compute(bq[d], d & 1);
-      workgroup_barrier();
-    }
 
   const int64_t col = n0 + fr;
   const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
