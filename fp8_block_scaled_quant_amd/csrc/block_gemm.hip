@@ -409,37 +409,44 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel for M <= 2 (decode), with or without the fused act_quant.
-// The weight B [n, k] is streamed from
-// HBM exactly once and dominates the traffic, so the kernel is built to keep
-// many weight bytes in flight with many waves.  A workgroup owns 16 * kNT
-// weight rows; its four waves split the K range four ways (partial sums meet
-// in LDS at the end), and each wave keeps the B fragments of its next kDepth
-// K blocks in registers, issuing the load for block kb + kDepth as it consumes
-// block kb.  A (at most 2 x k codes) is read through the caches as it is
-// used: holding its fragments in the ring too was measured slower, because the
-// extra registers halve the waves per SIMD.  The activation scales are staged
-// once per workgroup in LDS, transposed to [kb][row].  A wave's weight rows
-// lie in one 128-row weight block, so b_s is one scalar per K block.
-// kMT = ceil(m / 16) MFMA tiles cover the activation rows.
+// Decode kernel for M <= 64 (the weight B [n, k] streams from HBM once and
+// dominates the traffic).
+//
+// A workgroup owns 80 weight rows, one 16-row MFMA tile per compute wave
+// (waves 0-4), and all of them walk the same K blocks.  A sixth wave only
+// moves A: it DMAs each K block of A (16 kMT rows x 128 bytes, in whole-line
+// 16-byte pieces, with the XOR swizzle of the tiled kernel) and its kMT x 16
+// activation scales into an LDS ring of kDecode2Slots slots, kDecode2Lead
+// blocks ahead, waiting on its own transfers only, and one barrier per K block
+// hands the ring on.  The weight streams from HBM per compute wave (below), so
+// the only vector-memory transfers a compute wave waits on are its own weight
+// loads.  (A first design split K across four waves instead: every workgroup
+// then pulled all of A through fragment-shaped loads, and because a wave's
+// loads complete in order, each wait for an A fragment also drained its
+// weight prefetch ring; it was 20-45% slower at every M.)
+//
+// Fused act_quant (kFuseQ, M <= kFusedMaxM, bf16 activations): every
+// workgroup quantizes all of x [m, k] into LDS in its prologue with
+// act_quant's arithmetic, and workgroup 0 also publishes the codes and
+// scales; there is no mover and no per-block barrier.  The compute waves do
+// the same arithmetic in the same order as on the two-call path, so both give
+// bit-identical outputs.
 // ---------------------------------------------------------------------------
-constexpr int kDecodeWaves = 4, kDecodeMaxM = 64, kDecodeMaxKb = 160;
+constexpr int kDecodeMaxM = 64;
+// Longest K (in K blocks) of the fused path, whose scales sit in LDS for the
+// whole run.
+constexpr int kDecodeMaxKb = 160;
 // Activations quantized inside the decode kernel (fused act_quant) for up to
 // this many rows: every workgroup quantizes all of them, so the redundant work
-// grows with m: at m = 1 the one launch beats act_quant + GEMM by about 5%,
-// at m = 2 they tie, and at m = 4 two launches are faster.
+// grows with m.
 constexpr int kFusedMaxM = 2;
-// B ring depth of the single-tile (m <= 16) configuration: deep enough to keep
-// the weight stream busy, shallow enough (96 VGPRs) for five waves per SIMD, so
-// every workgroup of an N = 18432 launch is resident at once.
-constexpr int kDecodeDepth1 = 6;
 
 // Fused prologue: quantize x [m, k] bf16 (m <= kFusedMaxM) per 1 x 128 block
 // exactly as the act_quant kernel does -- sixteen lanes per block, 8 elements
 // each, amax over the 16-lane row, the same scale and quotient arithmetic --
 // into LDS codes aq [m][k] and scales as_t [kb][row].  Workgroup 0 also writes
 // the codes and scales to a_q / a_s_out, bit-identical to fp8_act_quant.
-template <int kRows>
+template <int kRows, int kThreadsQ>
 __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int m, int nkb,
                                                 bool ue8m0, uint8_t *aq, float (*as_t)[kRows],
                                                 uint8_t *__restrict__ a_q,
@@ -448,7 +455,7 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
   const int nblocks = m * nkb;                     // blocks of the flat [m * nkb, 128] sequence
   // the sixteen lanes of a block share its loop trip count, as the row
   // reduction needs
-  for (int blk = row16; blk < nblocks; blk += 64 * kDecodeWaves / 16) {
+  for (int blk = row16; blk < nblocks; blk += kThreadsQ / 16) {
     const u32x4 v = x[(int64_t)blk * 16 + sub];
     u16x2 m2 = {0, 0};
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
@@ -469,176 +476,6 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
   }
 }
 
-template <bool kBf16Out, int kMT, int kNT, int kDepth, bool kFuseQ = false>
-__global__ __launch_bounds__(64 * kDecodeWaves) void block_gemm_decode_kernel(
-    const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
-    const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
-    const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
-    float *__restrict__ a_s_out = nullptr) {
-  constexpr int kRows = 16 * kMT;
-  __shared__ float as_t[kDecodeMaxKb][kRows];   // [kb][row], zero-padded rows
-  __shared__ f32x4 red[kDecodeWaves - 1][kMT * kNT][64];
-  extern __shared__ __attribute__((aligned(16))) uint8_t aq[];   // fused: codes [m][k]
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int nkb = (int)(k / kBlock);
-  if constexpr (kFuseQ) {
-    // `a` holds the bf16 activations; rows m..kRows-1 of the scales stay 0
-    for (int i = t; i < nkb * kRows; i += 64 * kDecodeWaves) as_t[i / kRows][i % kRows] = 0.0f;
-    __syncthreads();
-    fused_act_quant<kRows>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q, a_s_out,
-                           blockIdx.x == 0);
-  } else {
-    // a_s [m, nkb] is read in its own (row-major, contiguous) order so the
-    // loads coalesce, eight per thread in flight before any LDS write, and
-    // transposed into as_t; rows m..kRows-1 are zero.
-    const int total = (int)m * nkb;
-    constexpr int kUnroll = 8, kStride = 64 * kDecodeWaves;
-    for (int base = 0; base < total; base += kStride * kUnroll) {
-      float v[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = base + kStride * u + t;
-        v[u] = i < total ? a_s[i] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = base + kStride * u + t;
-        if (i < total) as_t[i % nkb][i / nkb] = v[u];
-      }
-    }
-    for (int i = t; i < nkb * (kRows - (int)m); i += kStride) {
-      const int kb = i / (kRows - (int)m), r = (int)m + i % (kRows - (int)m);
-      as_t[kb][r] = 0.0f;
-    }
-  }
-  __syncthreads();
-
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * kNT;
-  const int fr = lane & 15, fq = lane >> 4;
-  const float *bs_row = b_s + (n0 / kBlock) * nkb;
-  const int kb_begin = wave * nkb / kDecodeWaves, kb_end = (wave + 1) * nkb / kDecodeWaves;
-  // lane -> (row fr, bytes [16 fq, 16 fq + 16) and [64 + 16 fq, ...)) of a K block;
-  // A and B use the same byte -> k assignment.
-  const uint8_t *b_src[kNT];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) b_src[nt] = b + min(n0 + 16 * nt + fr, n - 1) * k + 16 * fq;
-  const uint8_t *a_src[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) a_src[mt] = a + min((int64_t)(16 * mt + fr), m - 1) * k + 16 * fq;
-  // fused: rows past m are zero fragments, the others come from LDS
-  const bool a_row_live = fr < m;
-  const uint8_t *a_lds = aq + (int64_t)(a_row_live ? fr : 0) * k + 16 * fq;
-
-  auto load_frag = [&](const uint8_t *row, int kb) {
-    const uint8_t *p = row + (int64_t)kb * kBlock;
-    const uint4 lo = *(const uint4 *)p, hi = *(const uint4 *)(p + 64);
-    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  };
-
-  f32x4 acc[kMT][kNT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ring of the B fragments of the next kDepth K blocks
-  i32x8 bq[kDepth][kNT];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (kb_begin + d < kb_end)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) bq[d][nt] = load_frag(b_src[nt], kb_begin + d);
-
-  for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kDepth) {
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int kb = kb0 + d;
-      if (kb < kb_end) {
-        i32x8 bf[kNT];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          bf[nt] = bq[d][nt];
-          if (kb + kDepth < kb_end) bq[d][nt] = load_frag(b_src[nt], kb + kDepth);
-        }
-        const float sb = bs_row[kb];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          const f32x4 sa = *(const f32x4 *)&as_t[kb][16 * mt + 4 * fq];
-          i32x8 af;
-          if constexpr (kFuseQ) {
-            af = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (a_row_live) {
-              const uint4 lo = *(const uint4 *)(a_lds + (int64_t)kb * kBlock);
-              const uint4 hi = *(const uint4 *)(a_lds + (int64_t)kb * kBlock + 64);
-              af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            }
-          } else {
-            af = load_frag(a_src[mt], kb);
-          }
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) {
-            const f32x4 p = mfma_e4m3_16x16x128(af, bf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[mt][nt][e] = __builtin_fmaf(p[e], sa[e] * sb, acc[mt][nt][e]);
-          }
-        }
-      }
-    }
-  }
-
-  // waves 1..3 hand their partial sums to wave 0 through LDS
-  if (wave > 0) {
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) red[wave - 1][mt * kNT + nt][lane] = acc[mt][nt];
-  }
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < kDecodeWaves - 1; ++w)
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const f32x4 o = red[w][mt * kNT + nt][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[mt][nt][e] += o[e];
-      }
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const int64_t col = n0 + 16 * nt + fr;
-    const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = 16 * mt + 4 * fq + e;
-        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][nt][e] + bv);
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Decode kernel for 2 < M <= 64 (and smaller M when K is too long for the
-// kernel above).  Splitting K across the waves (above) makes every workgroup pull all
-// of A through fragment-shaped loads, twice the weight bytes it streams at
-// M = 64; and since a wave's loads complete in
-// order, each wait for an A fragment also waits for every older weight load in
-// the ring, which shortens the effective prefetch depth to a block or two.
-//
-// Here a workgroup owns 80 weight rows, one 16-row MFMA tile per compute wave
-// (waves 0-4), and all of them walk the same K blocks.  A sixth wave only
-// moves A: it DMAs each K block of A (16 kMT rows x 128 bytes, in whole-line
-// 16-byte pieces, with the XOR swizzle of the tiled kernel) and its kMT x 16
-// activation scales into an LDS ring of kDecode2Slots slots, kDecode2Lead
-// blocks ahead, waiting on its own transfers only.  The compute waves read A
-// fragments and scales from the ring and stream their weight fragments from
-// HBM through a kDepth-deep register ring, so the only vector-memory loads
-// they wait on are their own weight loads.  One barrier per K block hands the
-// ring on.
-// ---------------------------------------------------------------------------
 constexpr int kDecode2Compute = 5;                // compute waves per workgroup (plus the mover)
 constexpr int kDecode2Rows = 16 * kDecode2Compute;   // weight rows per workgroup
 constexpr int kDecode2Lead = 6;                   // K blocks of A in flight ahead of use
@@ -663,16 +500,21 @@ struct Decode2Slot {
 // kTabKb K blocks' scales per row, loaded one chunk ahead in 16-byte pieces;
 // otherwise each K block's kRows scales travel in its ring slot, one 4-byte
 // transfer per row.
-template <bool kBf16Out, int kMT, int kDepth, bool kTab>
-__global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2_kernel(
+template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false>
+__global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
-    const void *__restrict__ bias) {
+    const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
+    float *__restrict__ a_s_out = nullptr) {
+  static_assert(!kFuseQ || kMT == 1, "the fused path covers m <= kFusedMaxM");
   constexpr int kRows = 16 * kMT;
   constexpr int kDmaPerBlock = kRows / 8 + (kTab ? 0 : 1);   // A row groups of 8 (+ the scales)
   // table: [32-row block][half][row][4 K blocks], as the DMA lanes lay it down
   constexpr int kTabRows = (kRows + 31) / 32 * 32;   // whole 32-row blocks (one DMA each)
-  __shared__ __attribute__((aligned(1024))) Decode2Slot<kMT> ring[kDecode2Slots];
+  __shared__ __attribute__((aligned(1024))) Decode2Slot<kMT> ring[kFuseQ ? 1 : kDecode2Slots];
+  // fused: codes [m][k] (dynamic) and scales [kb][row] of all of x
+  extern __shared__ __attribute__((aligned(16))) uint8_t aq[];
+  __shared__ float as_t[kFuseQ ? kDecodeMaxKb : 1][kRows];
   __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
   // weight path: up to 32 activation rows each compute wave DMAs its weight
   // rows into an LDS ring (whole-line transfers, half the vector-memory issue
@@ -683,7 +525,7 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
                                                          [kBLds ? 16 * kBlock : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool mover = wave == kDecode2Compute;
+  const bool mover = !kFuseQ && wave == kDecode2Compute;
   const int nkb = (int)(k / kBlock);
 
   // mover: lane p of row group g fills chunk slot p % 8 of row 8 g + p / 8;
@@ -772,6 +614,14 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
   // branch-free: the compiler's count of weight loads in flight stays exact,
   // and no ring register is merged across paths (either would make it wait
   // for every load in flight).
+  if constexpr (kFuseQ) {
+    // `a` holds the bf16 activations; scale rows m..kRows-1 stay 0
+    for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kDecode2Compute) as_t[i / kRows][i % kRows] = 0.0f;
+    __syncthreads();
+    fused_act_quant<kRows, 64 * kDecode2Compute>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q,
+                                                 a_s_out, blockIdx.x == 0);
+    __syncthreads();
+  }
   if (mover) {
     // the compute waves read block kb + 1 while they compute kb, so by the
     // barrier that ends block kb, block kb + 2 must have landed
@@ -801,7 +651,21 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
   i32x8 af[2][kMT];
   f32x4 sa[2][kMT];
   float sb[2];
+  const bool a_row_live = fr < m;   // fused: rows past m are zero fragments
+  const uint8_t *a_lds = aq + (int64_t)(a_row_live ? fr : 0) * k + 16 * fq;
   auto read_a = [&](int kb, int buf) {   // kb may be nkb (a stale slot, never used)
+    if constexpr (kFuseQ) {
+      const int kbc = min(kb, nkb - 1);
+      af[buf][0] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (a_row_live) {
+        const uint4 lo = *(const uint4 *)(a_lds + (int64_t)kbc * kBlock);
+        const uint4 hi = *(const uint4 *)(a_lds + (int64_t)kbc * kBlock + 64);
+        af[buf][0] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      sa[buf][0] = *(const f32x4 *)&as_t[kbc][4 * fq];
+      sb[buf] = bs_row[kbc];
+      return;
+    }
     const Decode2Slot<kMT> &sl = ring[kb % kDecode2Slots];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
@@ -849,12 +713,12 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode2
       read_b(kb + 1, cur ^ 1);
       compute(bf[cur], cur);
       issue_b(min(kb + kDepth, nkb - 1));
-      workgroup_barrier();
+      if (!kFuseQ) workgroup_barrier();   // hands the mover's A ring on
     };
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) issue_b(min(d, nkb - 1));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kDepth - 1)) : "memory");
-    workgroup_barrier();
+    if (!kFuseQ) workgroup_barrier();
     read_a(0, 0);
     read_b(0, 0);
     const int neven = nkb & ~1;
@@ -934,34 +798,16 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
 #undef FP8BSQ_TILE
     return hipGetLastError();
   }
-  // K-split decode kernel up to the fused path's M, so that fp8_act_quant_gemm's
-  // one-kernel and two-call paths share their GEMM arithmetic
-  if (m <= kFusedMaxM && k / kBlock <= kDecodeMaxKb) {
-    const dim3 block(64 * kDecodeWaves);
-#define FP8BSQ_DECODE(MT, NT, D)                                                                 \
-  do {                                                                                           \
-    const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)));                                  \
-    if (c_bf16)                                                                                  \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, NT, D>), grid, block, 0, stream, a,  \
-                         a_s, b, b_s, c, m, n, k, bias);                                         \
-    else                                                                                         \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, NT, D>), grid, block, 0, stream, a, \
-                         a_s, b, b_s, c, m, n, k, bias);                                         \
-  } while (0)
-    FP8BSQ_DECODE(1, 1, kDecodeDepth1);
-#undef FP8BSQ_DECODE
-    return hipGetLastError();
-  }
   if (m <= kDecodeMaxM) {
     const dim3 grid((unsigned)((n + kDecode2Rows - 1) / kDecode2Rows)), block(64 * (kDecode2Compute + 1));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
 #define FP8BSQ_DECODE2_T(MT, TAB)                                                                          \
   do {                                                                                                     \
     if (c_bf16)                                                                                            \
-      hipLaunchKernelGGL((block_gemm_decode2_kernel<true, MT, kDecode2Depth, TAB>), grid, block, 0, stream, \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, kDecode2Depth, TAB>), grid, block, 0, stream, \
                          a, a_s, b, b_s, c, m, n, k, bias);                                                \
     else                                                                                                   \
-      hipLaunchKernelGGL((block_gemm_decode2_kernel<false, MT, kDecode2Depth, TAB>), grid, block, 0,        \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, kDecode2Depth, TAB>), grid, block, 0,        \
                          stream, a, a_s, b, b_s, c, m, n, k, bias);                                        \
   } while (0)
 #define FP8BSQ_DECODE2(MT)                                                                                 \
@@ -992,14 +838,15 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
                                       const float *b_s, const void *bias, void *c, bool c_bf16,
                                       int64_t m, int64_t n, int64_t k, uint8_t *a_q, float *a_s,
                                       hipStream_t stream) {
-  const dim3 grid((unsigned)((n + 15) / 16)), block(64 * kDecodeWaves);
+  // no mover: the compute waves only
+  const dim3 grid((unsigned)((n + kDecode2Rows - 1) / kDecode2Rows)), block(64 * kDecode2Compute);
   const size_t lds = (size_t)(m * k);
   if (c_bf16)
-    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, 1, kDecodeDepth1, true>), grid, block, lds, stream,
-                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
+    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecode2Depth, false, true>), grid, block, lds,
+                       stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
   else
-    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, 1, kDecodeDepth1, true>), grid, block, lds, stream,
-                       (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
+    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecode2Depth, false, true>), grid, block, lds,
+                       stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
   return hipGetLastError();
 }
 
