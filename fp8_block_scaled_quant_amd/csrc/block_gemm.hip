@@ -798,7 +798,9 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
 #undef FP8BSQ_TILE
     return hipGetLastError();
   }
-  if (m <= kDecodeMaxM) {
+  // the decode kernel's A and weight transfers use 32-bit lane offsets (from A's
+  // base, and from each wave's first weight row)
+  if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && 16 * k < ((int64_t)1 << 32)) {
     const dim3 grid((unsigned)((n + kDecode2Rows - 1) / kDecode2Rows)), block(64 * (kDecode2Compute + 1));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
 #define FP8BSQ_DECODE2_T(MT, TAB)                                                                          \
