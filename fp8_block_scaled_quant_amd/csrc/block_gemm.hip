@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 // (waves 0-4), and all of them walk the same K blocks.  A sixth wave only
 // moves A: it DMAs each K block of A (16 kMT rows x 128 bytes, in whole-line
 // 16-byte pieces, with the XOR swizzle of the tiled kernel) and its kMT x 16
-// activation scales into an LDS ring of kDecode2Slots slots, kDecode2Lead
+// activation scales into an LDS ring of kDecodeSlots slots, kDecodeLead
 // blocks ahead, waiting on its own transfers only, and one barrier per K block
 // hands the ring on.  The weight streams from HBM per compute wave (below), so
 // the only vector-memory transfers a compute wave waits on are its own weight
@@ -476,14 +476,14 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
   }
 }
 
-constexpr int kDecode2Compute = 5;                // compute waves per workgroup (plus the mover)
-constexpr int kDecode2Rows = 16 * kDecode2Compute;   // weight rows per workgroup
-constexpr int kDecode2Lead = 6;                   // K blocks of A in flight ahead of use
-constexpr int kDecode2Slots = kDecode2Lead + 1;   // LDS ring slots
-constexpr int kDecode2Depth = 6;                  // weight ring depth per compute wave (even)
+constexpr int kDecodeCompute = 5;                // compute waves per workgroup (plus the mover)
+constexpr int kDecodeRows = 16 * kDecodeCompute;   // weight rows per workgroup
+constexpr int kDecodeLead = 6;                   // K blocks of A in flight ahead of use
+constexpr int kDecodeSlots = kDecodeLead + 1;   // LDS ring slots
+constexpr int kDecodeDepth = 6;                  // weight ring depth per compute wave (even)
 
 template <int kMT>
-struct Decode2Slot {
+struct DecodeSlot {
   uint8_t a[16 * kMT * kBlock];   // [row][16-byte chunk slot], swizzled
   float s[16 * kMT];              // a_s of the K block, per row
 };
@@ -501,7 +501,7 @@ struct Decode2Slot {
 // otherwise each K block's kRows scales travel in its ring slot, one 4-byte
 // transfer per row.
 template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false>
-__global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_kernel(
+__global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
   constexpr int kDmaPerBlock = kRows / 8 + (kTab ? 0 : 1);   // A row groups of 8 (+ the scales)
   // table: [32-row block][half][row][4 K blocks], as the DMA lanes lay it down
   constexpr int kTabRows = (kRows + 31) / 32 * 32;   // whole 32-row blocks (one DMA each)
-  __shared__ __attribute__((aligned(1024))) Decode2Slot<kMT> ring[kFuseQ ? 1 : kDecode2Slots];
+  __shared__ __attribute__((aligned(1024))) DecodeSlot<kMT> ring[kFuseQ ? 1 : kDecodeSlots];
   // fused: codes [m][k] (dynamic) and scales [kb][row] of all of x
   extern __shared__ __attribute__((aligned(16))) uint8_t aq[];
   __shared__ float as_t[kFuseQ ? kDecodeMaxKb : 1][kRows];
@@ -521,11 +521,11 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
   // of fragment-shaped loads); above that the waves' A-fragment reads already
   // load the LDS heavily, and the weight fragments stream into registers
   constexpr bool kBLds = kMT <= 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t bring[kBLds ? kDecode2Compute : 1][kBLds ? kDepth : 1]
+  __shared__ __attribute__((aligned(1024))) uint8_t bring[kBLds ? kDecodeCompute : 1][kBLds ? kDepth : 1]
                                                          [kBLds ? 16 * kBlock : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool mover = !kFuseQ && wave == kDecode2Compute;
+  const bool mover = !kFuseQ && wave == kDecodeCompute;
   const int nkb = (int)(k / kBlock);
 
   // mover: lane p of row group g fills chunk slot p % 8 of row 8 g + p / 8;
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
   const uint32_t s_off = (uint32_t)(min((int64_t)lane, m - 1) * nkb * 4);
   const uint32_t lds_ring = lds_addr(&ring[0]);
   auto issue = [&](int kb) {
-    const uint32_t slot = lds_ring + (uint32_t)((kb % kDecode2Slots) * sizeof(Decode2Slot<kMT>));
+    const uint32_t slot = lds_ring + (uint32_t)((kb % kDecodeSlots) * sizeof(DecodeSlot<kMT>));
 #pragma unroll
     for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
     if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + kRows * kBlock);
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
   };
   // wait until a K block's transfers have landed, given how many blocks were
   // issued after it (transfers complete in issue order)
-  static_assert(kDecode2Lead == 6 && 5 * kDmaPerBlock < 64, "one vmcnt case per block behind");
+  static_assert(kDecodeLead == 6 && 5 * kDmaPerBlock < 64, "one vmcnt case per block behind");
   auto wait_block = [&](int behind) {
     switch (behind) {
       case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * kDmaPerBlock) : "memory"); break;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
     }
   };
 
-  const int64_t n0 = (int64_t)blockIdx.x * kDecode2Rows + 16 * (mover ? 0 : wave);
+  const int64_t n0 = (int64_t)blockIdx.x * kDecodeRows + 16 * (mover ? 0 : wave);
   const int fr = lane & 15, fq = lane >> 4;
   const float *bs_row = b_s + min(n0 / kBlock, (n - 1) / kBlock) * nkb;
   // kBLds: each compute wave DMAs its own 16 weight rows of a K block (two
@@ -616,9 +616,9 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
   // for every load in flight).
   if constexpr (kFuseQ) {
     // `a` holds the bf16 activations; scale rows m..kRows-1 stay 0
-    for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kDecode2Compute) as_t[i / kRows][i % kRows] = 0.0f;
+    for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kDecodeCompute) as_t[i / kRows][i % kRows] = 0.0f;
     __syncthreads();
-    fused_act_quant<kRows, 64 * kDecode2Compute>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q,
+    fused_act_quant<kRows, 64 * kDecodeCompute>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q,
                                                  a_s_out, blockIdx.x == 0);
     __syncthreads();
   }
@@ -626,17 +626,17 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
     // the compute waves read block kb + 1 while they compute kb, so by the
     // barrier that ends block kb, block kb + 2 must have landed
     if (kTab) issue_tab(0);
-    for (int kb = 0; kb < kDecode2Lead && kb < nkb; ++kb) issue(kb);
-    wait_block(min(kDecode2Lead, nkb) - 1 - min(1, nkb - 1));
+    for (int kb = 0; kb < kDecodeLead && kb < nkb; ++kb) issue(kb);
+    wait_block(min(kDecodeLead, nkb) - 1 - min(1, nkb - 1));
     workgroup_barrier();
     for (int kb = 0; kb < nkb; ++kb) {
       // the slot of kb + lead was last read during block kb - 2
-      if (kb + kDecode2Lead < nkb) issue(kb + kDecode2Lead);
+      if (kb + kDecodeLead < nkb) issue(kb + kDecodeLead);
       // chunk c + 1 into the buffer chunk c - 1 used (last read during block
       // kb - 2); it is older than block kb + 7's transfers, which are waited
       // for (two blocks ahead of their use) before its first read
       if (kTab && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
-      if (kb + 2 < nkb) wait_block(min(kb + kDecode2Lead, nkb - 1) - (kb + 2));
+      if (kb + 2 < nkb) wait_block(min(kb + kDecodeLead, nkb - 1) - (kb + 2));
       workgroup_barrier();
     }
     wait_dma_all();
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(64 * (kDecode2Compute + 1)) void block_gemm_decode_
       sb[buf] = bs_row[kbc];
       return;
     }
-    const Decode2Slot<kMT> &sl = ring[kb % kDecode2Slots];
+    const DecodeSlot<kMT> &sl = ring[kb % kDecodeSlots];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
       const uint4 lo = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_lo]);
@@ -801,29 +801,29 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   // the decode kernel's A and weight transfers use 32-bit lane offsets (from A's
   // base, and from each wave's first weight row)
   if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && 16 * k < ((int64_t)1 << 32)) {
-    const dim3 grid((unsigned)((n + kDecode2Rows - 1) / kDecode2Rows)), block(64 * (kDecode2Compute + 1));
+    const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * (kDecodeCompute + 1));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
-#define FP8BSQ_DECODE2_T(MT, TAB)                                                                          \
+#define FP8BSQ_DECODE_T(MT, TAB)                                                                          \
   do {                                                                                                     \
     if (c_bf16)                                                                                            \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, kDecode2Depth, TAB>), grid, block, 0, stream, \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, kDecodeDepth, TAB>), grid, block, 0, stream, \
                          a, a_s, b, b_s, c, m, n, k, bias);                                                \
     else                                                                                                   \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, kDecode2Depth, TAB>), grid, block, 0,        \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, kDecodeDepth, TAB>), grid, block, 0,        \
                          stream, a, a_s, b, b_s, c, m, n, k, bias);                                        \
   } while (0)
-#define FP8BSQ_DECODE2(MT)                                                                                 \
+#define FP8BSQ_DECODE(MT)                                                                                 \
   do {                                                                                                     \
-    if (tab) FP8BSQ_DECODE2_T(MT, true); else FP8BSQ_DECODE2_T(MT, false);                                 \
+    if (tab) FP8BSQ_DECODE_T(MT, true); else FP8BSQ_DECODE_T(MT, false);                                 \
   } while (0)
     switch ((m + 15) / 16) {
-      case 1: FP8BSQ_DECODE2(1); break;
-      case 2: FP8BSQ_DECODE2(2); break;
-      case 3: FP8BSQ_DECODE2(3); break;
-      default: FP8BSQ_DECODE2(4); break;
+      case 1: FP8BSQ_DECODE(1); break;
+      case 2: FP8BSQ_DECODE(2); break;
+      case 3: FP8BSQ_DECODE(3); break;
+      default: FP8BSQ_DECODE(4); break;
     }
-#undef FP8BSQ_DECODE2
-#undef FP8BSQ_DECODE2_T
+#undef FP8BSQ_DECODE
+#undef FP8BSQ_DECODE_T
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), block(256);
@@ -841,13 +841,13 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
                                       int64_t m, int64_t n, int64_t k, uint8_t *a_q, float *a_s,
                                       hipStream_t stream) {
   // no mover: the compute waves only
-  const dim3 grid((unsigned)((n + kDecode2Rows - 1) / kDecode2Rows)), block(64 * kDecode2Compute);
+  const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * kDecodeCompute);
   const size_t lds = (size_t)(m * k);
   if (c_bf16)
-    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecode2Depth, false, true>), grid, block, lds,
+    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecodeDepth, false, true>), grid, block, lds,
                        stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
   else
-    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecode2Depth, false, true>), grid, block, lds,
+    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecodeDepth, false, true>), grid, block, lds,
                        stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
   return hipGetLastError();
 }
