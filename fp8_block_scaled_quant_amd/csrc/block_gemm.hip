@@ -772,12 +772,20 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
 
 }  // namespace
 
+// Diagnostic: FP8BSQ_GEMM_REFERENCE=1 in the environment sends every GEMM to
+// the reference-structure kernel (read on each call).
+static bool reference_kernel_forced() {
+  const char *v = getenv("FP8BSQ_GEMM_REFERENCE");
+  return v && v[0] == '1';
+}
+
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream, const void *bias, bool a_s_pow2) {
+  const bool reference = reference_kernel_forced();
   // the tiled kernel addresses A, B and a_s with 32-bit per-lane offsets
   const bool offsets_fit = m * k < ((int64_t)1 << 32) && n * k < ((int64_t)1 << 32);
-  if (m > 64 && offsets_fit) {
+  if (!reference && m > 64 && offsets_fit) {
     const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
 #define FP8BSQ_TILE(BF16, MX, TAB)                                                                   \
@@ -800,7 +808,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   }
   // the decode kernel's A and weight transfers use 32-bit lane offsets (from A's
   // base, and from each wave's first weight row)
-  if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && 16 * k < ((int64_t)1 << 32)) {
+  if (!reference && m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && 16 * k < ((int64_t)1 << 32)) {
     const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * (kDecodeCompute + 1));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
 #define FP8BSQ_DECODE_T(MT, TAB)                                                                          \

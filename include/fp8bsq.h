@@ -154,6 +154,9 @@ FP8BSQ_API int fp8_weight_quant(const void *x, int x_dtype, int64_t m, int64_t n
  *
  * Accumulation order is not specified; every element is within
  * 1e-3 * sum_k |a_k * b_k| of the exact result (plus one bf16 ulp for BF16).
+ * Diagnostic: with FP8BSQ_GEMM_REFERENCE=1 in the environment (read on each
+ * call) every GEMM entry point uses the slow reference-structure kernel that
+ * otherwise serves only shapes beyond the fast kernels' 32-bit offsets.
  */
 FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
                    void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream);

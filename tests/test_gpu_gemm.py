@@ -120,6 +120,19 @@ def test_scale_indexing_probe_tiled(m, aligned):
     _assert_close(got, a, a_s, b, b_s, "f32", label="tiled scale probe")
 
 
+@pytest.mark.parametrize("m,n,k", [(3, 200, 384), (100, 300, 1024), (257, 130, 640)])
+def test_reference_kernel(m, n, k, monkeypatch):
+    """The reference-structure kernel (what shapes beyond the tiled and decode
+    kernels' 32-bit offsets take), forced by FP8BSQ_GEMM_REFERENCE=1."""
+    monkeypatch.setenv("FP8BSQ_GEMM_REFERENCE", "1")
+    d = gen.custom_gemm(seed=5 * m + n, m=m, n=n, k=k, outliers=True)
+    G.announce(f"gemm reference kernel m={m} n={n} k={k}")
+    a, a_s = _quantized_activations(d["x"], None)
+    for out in ("bf16", "f32"):
+        got = G.block_gemm(a, a_s, d["w"], d["w_s"], out)
+        _assert_close(got, a, a_s, d["w"], d["w_s"], out, label=f"reference {m}x{n}x{k}")
+
+
 def test_python_binding_end_to_end():
     from fp8_block_scaled_quant_amd import act_quant, fp8_gemm
     d = gen.custom_gemm(seed=5, m=40, n=256, k=512)
