@@ -95,13 +95,24 @@ def test_python_binding():
     (3, 256, 20608, "bf16"),     # long K with K/128 = 161: no scale table
 ])
 def test_bias_in_epilogue(m, n, k, out):
+    _bias_case(m, n, k, out, None)
+
+
+# ue8m0 scales through the tiled GEMM: the MX-scaled kernel's epilogue, with
+# ragged N and M
+@pytest.mark.parametrize("m,n,k,out", [(300, 700, 1024, "bf16"), (257, 450, 512, "f32")])
+def test_bias_in_epilogue_ue8m0_tiled(m, n, k, out):
+    _bias_case(m, n, k, out, "ue8m0")
+
+
+def _bias_case(m, n, k, out, scale_fmt):
     d = gen.custom_gemm(seed=m + n + k, m=m, n=n, k=k)
-    G.announce(f"act_quant_gemm bias m={m} n={n} k={k} out={out}")
+    G.announce(f"act_quant_gemm bias m={m} n={n} k={k} out={out} scale_fmt={scale_fmt}")
     dtype = torch.bfloat16 if out == "bf16" else torch.float32
     bias = torch.from_numpy(np.random.default_rng(m).standard_normal(n).astype(np.float32) * 4).to(dtype)
-    got, codes, scales = G.act_quant_gemm(d["x"].to(G.device()), d["w"], d["w_s"], None, out,
+    got, codes, scales = G.act_quant_gemm(d["x"].to(G.device()), d["w"], d["w_s"], scale_fmt, out,
                                           bias=bias.to(G.device()))
-    wq, ws = oracle.act_quant(d["x"].float().numpy(), 128, None)
+    wq, ws = oracle.act_quant(d["x"].float().numpy(), 128, scale_fmt)
     assert np.array_equal(codes, wq) and np.array_equal(scales.view(np.uint32), ws.view(np.uint32))
     c = oracle.fp8_gemm(wq, ws, d["w"], d["w_s"]) + bias.float().double().numpy()[None, :]
     tol = oracle.gemm_tolerance(wq, ws, d["w"], d["w_s"])

@@ -45,9 +45,11 @@ def test_prefill_workloads(shape):
 
 # K = 2560 and 1536: several 8-K-block scale-table chunks, the last one half
 # filled; K = 512: a single half-filled chunk; K = 768 and 128: K/128 not a
-# multiple of 4, which takes the generic kernel.
+# multiple of 4, which takes the generic kernel.  1100 x 7168: 140 tiles,
+# ragged in M, with several per XCD.
 @pytest.mark.parametrize("m,n,k,out", [(100, 300, 1024, "bf16"), (257, 385, 512, "f32"),
                                        (300, 260, 2560, "bf16"), (513, 256, 1536, "f32"),
+                                       (1100, 7168, 1024, "bf16"),
                                        (260, 300, 768, "bf16"),
                                        (65, 129, 128, "bf16"), (8, 500, 640, "f32")])
 def test_shapes(m, n, k, out):
