@@ -144,11 +144,15 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 // wave-uniform 64-bit base, so advancing to the next K block costs scalar adds
 // only.
 //
-// Only waves 0-3 issue the DMA, each for itself and for the wave that shares
-// its SIMD (w + 4).  The CU accepts these transfers at about one instruction
-// per 16-18 cycles, so the 64 issued at the top of a K block keep the issuing
-// wave waiting for most of a thousand cycles; with one issuer per SIMD the
-// other wave computes meanwhile instead of queueing behind it.
+// The CU accepts these transfers at about one instruction per 16-18 cycles,
+// and a wave that issues them waits until they are accepted, so where they
+// are issued decides who waits.  The next K block's A (32 instructions) is
+// issued by waves 0-3 at the top of the block, while waves 4-7 (one per SIMD)
+// start computing; its B (32) by all eight waves, four each, after their
+// first two columns of MFMAs, by which time the A transfers have been
+// accepted and the waves have MFMAs in flight.  B still lands well before the
+// next block's wait.  (All 64 issued at the top by waves 0-3 kept those waves
+// out of the matrix pipe for ~1,160 cycles per block and was 3% slower.)
 //
 // Activation scales (kTab): the kernel keeps a table of kTabKb K blocks'
 // scales per row, loaded in 16-byte pieces one chunk ahead (double-buffered).
@@ -245,19 +249,23 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
   const int64_t grid_n = (n + kBlock - 1) / kBlock;
   const float *bs_row = b_s + min((n0 + wn) / kBlock, grid_n - 1) * nkb;
 
-  // DMA plan: issuing wave d = wave (0..3) covers the 8-row groups
-  // g = d + 4 h + 8 i (h < 2, i < 4) of A and of B; lane p of a group fills
-  // slot p (row 8 g + p / 8, chunk slot p % 8).  Rows past the matrix edge
-  // re-read the last row; their outputs are never stored.
+  // DMA plan, in 8-row groups (one instruction each; lane p of a group fills
+  // slot p: row 8 g + p / 8, chunk slot p % 8): A group 8 d + g (g < 8) by
+  // wave d < 4, B group 4 w + h (h < 4) by every wave w.  Rows past the matrix
+  // edge re-read the last row; their outputs are never stored.
   const bool dma_wave = wave < 4;
   const int dw = wave & 3;
   const int dr = lane >> 3, ds = lane & 7;
-  uint32_t a_off[8], b_off[8];
+  uint32_t a_off[8], b_off[4];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {   // g = 4 i + h
-    const int row = 8 * (dw + 4 * (g & 1) + 8 * (g >> 1)) + dr;
+  for (int g = 0; g < 8; ++g) {
+    const int row = 8 * (8 * dw + g) + dr;
     a_off[g] = (uint32_t)(min(m0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
-    b_off[g] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int row = 8 * (4 * wave + h) + dr;
+    b_off[h] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
   }
   // scales of the 32-row blocks dw and dw + 4: generic, lanes 0..31 -> rows;
   // table, lane p -> row p % 32 and K blocks 4 (p / 32) .. +3 of the chunk
@@ -270,20 +278,24 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
   const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]),
                  lds_s = lds_addr(&sm.as[0][0]);
 
-  auto issue = [&](int kb, int s) {
+  // K block kb's A (and, without the table, its scales) into stage s: waves 0-3
+  auto issue_a = [&](int kb, int s) {
     const uint8_t *ab = a + (int64_t)kb * kBlock;
-    const uint8_t *bb = b + (int64_t)kb * kBlock;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int grp = dw + 4 * (g & 1) + 8 * (g >> 1);
-      lds_dma16(ab, a_off[g], lds_a + s * (kTileM * kBlock) + grp * 1024);
-      lds_dma16(bb, b_off[g], lds_b + s * (kTileN * kBlock) + grp * 1024);
-    }
+    for (int g = 0; g < 8; ++g)
+      lds_dma16(ab, a_off[g], lds_a + s * (kTileM * kBlock) + (8 * dw + g) * 1024);
     if (!kTab) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         if (lane < 32) lds_dma4(a_s + kb, s_off[h], lds_s + s * (kTileM * 4) + 32 * (dw + 4 * h) * 4);
     }
+  };
+  // K block kb's B into stage s: every wave
+  auto issue_b = [&](int kb, int s) {
+    const uint8_t *bb = b + (int64_t)kb * kBlock;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      lds_dma16(bb, b_off[h], lds_b + s * (kTileN * kBlock) + (4 * wave + h) * 1024);
   };
   // chunk c of the scale table (K blocks kTabKb c ..), into buffer c & 1; in
   // a last, half-filled chunk the upper lanes re-read their row's first four
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     wait_dma_all();
     workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
     if (dma_wave) {
-      if (kb + 1 < nkb) issue(kb + 1, cur ^ 1);
+      if (kb + 1 < nkb) issue_a(kb + 1, cur ^ 1);
       // the table buffer of chunk c + 1 was last read in chunk c - 1
       if (kTab && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
     }
@@ -364,6 +376,10 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
         const int q = 4 * j + i;
         part[q % 4] = kMxA ? mfma_e4m3_16x16x128_mx(af[i], bcur, ea[i])
                            : mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
+        // the next block's B, unconditionally so that no branch splits the
+        // unrolled loop (the last block re-reads itself into the stage no one
+        // reads again; drained after the loop)
+        if (j == 2 && i == 0) issue_b(min(kb + 1, nkb - 1), cur ^ 1);
         if (q >= 3) {
           const int qp = q - 3, ip = qp % 4, jp = qp / 4;
           if (!kMxA && qp < 4) {
@@ -388,11 +404,13 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
   };
 
   if (dma_wave) {
-    issue(0, 0);
+    issue_a(0, 0);
     if (kTab) issue_tab(0);
   }
+  issue_b(0, 0);
 #pragma nounroll
   for (int kb = 0; kb < nkb; ++kb) step(kb, kb & 1);
+  wait_dma_all();
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
