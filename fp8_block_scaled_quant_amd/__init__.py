@@ -142,13 +142,17 @@ def weight_quant(w: torch.Tensor, block_size: int = 128, scale_fmt=None):
 
 
 def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
-             out_dtype: torch.dtype = torch.bfloat16, scale_fmt=None) -> torch.Tensor:
+             out_dtype: torch.dtype = torch.bfloat16, scale_fmt=None, split: bool = True) -> torch.Tensor:
     """Block-scaled FP8 GEMM ``C = A . B^T`` (B is the [out, in] weight).
 
     ``a`` [..., K] E4M3 with ``a_s`` [..., K/128]; ``b`` [N, K] E4M3 with
     ``b_s`` [ceil(N/128), K/128].  Returns ``[..., N]`` in ``out_dtype``.
     ``scale_fmt="ue8m0"`` states that every a_s is a power of two (act_quant's
     ue8m0 scales) and selects the entry point that applies them in the MFMA.
+    ``split`` (default) lets a last round of output tiles that would leave
+    compute units idle run split over K (fp8_block_gemm_split, with a workspace
+    from torch's allocator); results then differ from ``split=False`` only in
+    FP32 summation order.
     """
     if scale_fmt not in _SCALE_FMT:
         raise ValueError(f"unknown scale_fmt {scale_fmt!r}")
@@ -171,11 +175,20 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Ten
         raise ValueError("b_s must be [ceil(N/128), K/128]")
     c = torch.empty(tuple(a.shape[:-1]) + (n,), dtype=out_dtype, device=a.device)
     if m and n:
-        fn = _lib.lib().fp8_block_gemm_ue8m0 if scale_fmt == "ue8m0" else _lib.lib().fp8_block_gemm
-        _lib.check(fn(
-            ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(a_s.data_ptr()),
-            ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),
-            ctypes.c_void_p(c.data_ptr()), _DTYPE[out_dtype], m, n, k, _stream_handle(a)))
+        lib = _lib.lib()
+        args = (ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(a_s.data_ptr()),
+                ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),
+                ctypes.c_void_p(c.data_ptr()), _DTYPE[out_dtype], m, n, k)
+        ws_bytes = lib.fp8_block_gemm_split_workspace(m, n, k) if split else 0
+        if ws_bytes:
+            # scratch for the split-K tail; torch's allocator keeps it from being
+            # reused until the work queued on this stream has passed it
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
+            _lib.check(lib.fp8_block_gemm_split(*args, _SCALE_FMT[scale_fmt], ctypes.c_void_p(ws.data_ptr()),
+                                                ws_bytes, _stream_handle(a)))
+        else:
+            fn = lib.fp8_block_gemm_ue8m0 if scale_fmt == "ue8m0" else lib.fp8_block_gemm
+            _lib.check(fn(*args, _stream_handle(a)))
     return c
 
 

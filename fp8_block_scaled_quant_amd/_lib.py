@@ -16,7 +16,8 @@ SCALE_NONE, SCALE_UE8M0 = 0, 1
 
 # every symbol include/fp8bsq.h declares
 EXPORTS = ("fp8_act_quant", "fp8_weight_dequant", "fp8_weight_quant", "fp8_block_gemm",
-           "fp8_block_gemm_ue8m0", "fp8_act_quant_gemm", "fp8bsq_strerror", "fp8bsq_version")
+           "fp8_block_gemm_ue8m0", "fp8_block_gemm_split", "fp8_block_gemm_split_workspace",
+           "fp8_act_quant_gemm", "fp8bsq_strerror", "fp8bsq_version")
 
 _LIB = None
 
@@ -52,6 +53,11 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.fp8_block_gemm.restype = i32
     lib.fp8_block_gemm_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     lib.fp8_block_gemm_ue8m0.restype = i32
+    lib.fp8_block_gemm_split.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp,
+                                         ctypes.c_size_t, vp]
+    lib.fp8_block_gemm_split.restype = i32
+    lib.fp8_block_gemm_split_workspace.argtypes = [i64, i64, i64]
+    lib.fp8_block_gemm_split_workspace.restype = ctypes.c_size_t
     lib.fp8_act_quant_gemm.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, vp]
     lib.fp8_act_quant_gemm.restype = i32
     lib.fp8bsq_strerror.argtypes = [i32]

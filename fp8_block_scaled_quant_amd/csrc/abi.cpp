@@ -1,5 +1,6 @@
 // C ABI of the block-scaled FP8 library: argument validation and dispatch.
 // Every check runs before any HIP call, so a rejected call queues nothing.
+#include <stddef.h>
 #include <stdint.h>
 
 #include "fp8bsq.h"
@@ -89,6 +90,29 @@ int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const f
 int fp8_block_gemm_ue8m0(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
                          void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
   return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream, true);
+}
+
+size_t fp8_block_gemm_split_workspace(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0) return 0;
+  if (m > kMaxGemmRows || n >= kMaxDim || k >= kMaxDim) return 0;
+  return fp8bsq::block_gemm_split_bytes(m, n, k);
+}
+
+int fp8_block_gemm_split(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
+                         void *c, int c_dtype, int64_t m, int64_t n, int64_t k, int scale_fmt,
+                         void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (!a || !a_s || !b || !b_s || !c) return FP8BSQ_EINVAL;
+  if (m <= 0 || n <= 0 || k <= 0) return FP8BSQ_EINVAL;
+  if (c_dtype != FP8BSQ_F32 && c_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
+  if (scale_fmt != FP8BSQ_SCALE_NONE && scale_fmt != FP8BSQ_SCALE_UE8M0) return FP8BSQ_EINVAL;
+  if (k % 128 != 0) return FP8BSQ_ESHAPE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
+      !aligned(c, 4) || !aligned(workspace, 256))
+    return FP8BSQ_EALIGN;
+  if (m > kMaxGemmRows || n >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
+  return launch_status(fp8bsq::launch_block_gemm_split(
+      a, a_s, b, b_s, c, c_dtype == FP8BSQ_BF16, m, n, k, (hipStream_t)hip_stream,
+      scale_fmt == FP8BSQ_SCALE_UE8M0, workspace, workspace ? workspace_bytes : 0));
 }
 
 int fp8_act_quant_gemm(const void *x, int x_dtype, int scale_fmt, const uint8_t *b,

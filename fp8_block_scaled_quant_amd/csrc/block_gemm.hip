@@ -181,6 +181,9 @@ constexpr int kTileM = 256, kTileN = 256, kThreads = 512;
 // K blocks per chunk of the power-of-two scale table
 constexpr int kTabKb = 8;
 
+// most parts a split-K tile is computed in
+constexpr int kSplitMax = 4;
+
 struct TileSmem {
   uint8_t a[2][kTileM * kBlock];
   uint8_t b[2][kTileN * kBlock];
@@ -233,18 +236,51 @@ __device__ __forceinline__ i32x8 frag_from_lds(const uint8_t *row_base, int fq, 
   return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <bool kBf16Out, bool kMxA, bool kTab>
+// kSplit: this launch computes tiles tile0, tile0 + 1, ... of the tile order,
+// each in nsplit parts over consecutive K ranges.  Every part stores its FP32
+// partial tile to ws, then counts itself in counters[tile] (zeroed by an
+// earlier launch on the stream); the part that counts last adds the partials
+// in part order (P0 + P1 + ...) and finishes the tile as the unsplit kernel
+// would.  No workgroup waits for another.  Unsplit launches with zero_n > 0
+// have workgroup 0 clear zero_ptr[0, zero_n) for a split launch that follows.
+template <bool kBf16Out, bool kMxA, bool kTab, bool kSplit = false>
 __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
-    int tiles_m, int tiles_n, const void *__restrict__ bias) {
+    int tiles_m, int tiles_n, const void *__restrict__ bias, int tile0 = 0, int nsplit = 1,
+    float *__restrict__ ws = nullptr, uint32_t *__restrict__ counters = nullptr,
+    uint32_t *__restrict__ zero_ptr = nullptr, int zero_n = 0) {
   __shared__ __attribute__((aligned(1024))) TileSmem sm;
+  if (!kSplit && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < zero_n; i += kThreads) zero_ptr[i] = 0u;
+  __shared__ int split_last;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
   const int nkb = (int)(k / kBlock);
+  int tm, tn, tslot = 0, part = 0, kb_begin = 0, kb_end = nkb;
+  if (kSplit) {
+    // Workgroups are dealt to the 8 XCDs round-robin.  With whole XCD shares
+    // of the tail, workgroup w of XCD w % 8 takes tile 8 u + w % 8 of the
+    // tail (its home XCD in the tile order, next to the tiles it shares A and
+    // B rows with) and part (w / 8) / (tail / 8): that XCD's tiles, part by part.
+    const int ntail = gridDim.x / nsplit;
+    if (ntail % 8 == 0 && tile0 % 8 == 0) {
+      const int local = blockIdx.x / 8, per = ntail / 8;
+      part = local / per;
+      tslot = 8 * (local % per) + blockIdx.x % 8;
+    } else {
+      tslot = blockIdx.x / nsplit;
+      part = blockIdx.x % nsplit;
+    }
+    // whole chunks of the scale table per part
+    const int per = ((nkb + kTabKb - 1) / kTabKb + nsplit - 1) / nsplit * kTabKb;
+    kb_begin = min(nkb, part * per);
+    kb_end = min(nkb, kb_begin + per);
+    tile_coords(tile0 + tslot, tiles_m, tiles_n, tm, tn);
+  } else {
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  }
+  const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
   const int64_t grid_n = (n + kBlock - 1) / kBlock;
   const float *bs_row = b_s + min((n0 + wn) / kBlock, grid_n - 1) * nkb;
@@ -321,9 +357,9 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     wait_dma_all();
     workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
     if (dma_wave) {
-      if (kb + 1 < nkb) issue_a(kb + 1, cur ^ 1);
+      if (kb + 1 < kb_end) issue_a(kb + 1, cur ^ 1);
       // the table buffer of chunk c + 1 was last read in chunk c - 1
-      if (kTab && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
+      if (kTab && kb % kTabKb == 0 && kb + kTabKb < kb_end) issue_tab(kb / kTabKb + 1);
     }
     // Retire the scalar load now (the empty asm consumes its value): scalar and
     // LDS results share one counter and the scalar one may return out of order,
@@ -379,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
         // the next block's B, unconditionally so that no branch splits the
         // unrolled loop (the last block re-reads itself into the stage no one
         // reads again; drained after the loop)
-        if (j == 2 && i == 0) issue_b(min(kb + 1, nkb - 1), cur ^ 1);
+        if (j == 2 && i == 0) issue_b(min(kb + 1, kb_end - 1), cur ^ 1);
         if (q >= 3) {
           const int qp = q - 3, ip = qp % 4, jp = qp / 4;
           if (!kMxA && qp < 4) {
@@ -404,13 +440,50 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
   };
 
   if (dma_wave) {
-    issue_a(0, 0);
-    if (kTab) issue_tab(0);
+    issue_a(kb_begin, 0);
+    if (kTab) issue_tab(kb_begin / kTabKb);
   }
-  issue_b(0, 0);
+  issue_b(kb_begin, 0);
 #pragma nounroll
-  for (int kb = 0; kb < nkb; ++kb) step(kb, kb & 1);
+  for (int kb = kb_begin; kb < kb_end; ++kb) step(kb, (kb - kb_begin) & 1);
   wait_dma_all();
+
+  if (kSplit) {
+    // partials in the lanes' own order: [tile][part][wave][i][j][lane][4]
+    const size_t tile_floats = (size_t)kTileM * kTileN;
+    float *base = ws + (size_t)tslot * nsplit * tile_floats + (size_t)wave * (tile_floats / 8) + lane * 4;
+    float *mine = base + (size_t)part * tile_floats;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *(f32x4 *)(mine + (i * 8 + j) * 256) = acc[i][j];
+    // Every wave's stores complete (in L2) before the barrier; one device-scope
+    // fence then publishes the workgroup's partial ahead of its count, and the
+    // last part's fence makes the others' partials visible before it reads
+    // them.  (Each fence writes back or invalidates a whole L2, so one per
+    // workgroup, not one per thread.)
+    wait_dma_all();
+    __syncthreads();
+    if (t == 0) {
+      __threadfence();
+      split_last = atomicAdd(&counters[tslot], 1u) == (uint32_t)(nsplit - 1);
+      if (split_last) __threadfence();
+    }
+    __syncthreads();
+    if (!split_last) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // every part from the workspace, this one's included: a select
+        // between acc and a load would pin acc to memory for the whole kernel
+        f32x4 sum = *(const f32x4 *)(base + (i * 8 + j) * 256);
+#pragma unroll
+        for (int p = 1; p < kSplitMax; ++p)
+          if (p < nsplit) sum += *(const f32x4 *)(base + (size_t)p * tile_floats + (i * 8 + j) * 256);
+        acc[i][j] = sum;
+      }
+  }
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -797,32 +870,118 @@ static bool reference_kernel_forced() {
   return v && v[0] == '1';
 }
 
+// the tiled kernel serves m > 64 while A, B and a_s fit its 32-bit per-lane offsets
+static bool tiled_path(int64_t m, int64_t n, int64_t k) {
+  return !reference_kernel_forced() && m > 64 && m * k < ((int64_t)1 << 32) &&
+         n * k < ((int64_t)1 << 32);
+}
+
+// Tiled kernel over `grid` workgroups (see block_gemm_tile_kernel for tile0,
+// nsplit, ws and counters; split selects the split-K instantiation).
+static hipError_t launch_tiles(const uint8_t *a, const float *a_s, const uint8_t *b,
+                               const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                               int64_t k, hipStream_t stream, const void *bias, bool a_s_pow2,
+                               unsigned grid, bool split, int tile0, int nsplit, float *ws,
+                               uint32_t *counters, int zero_n = 0) {
+  const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
+  const dim3 block(kThreads);
+#define FP8BSQ_TILE(BF16, MX, TAB)                                                                      \
+  do {                                                                                                   \
+    if (split)                                                                                           \
+      hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX, TAB, true>), dim3(grid), block, 0, stream, a, \
+                         a_s, b, b_s, c, m, n, k, tiles_m, tiles_n, bias, tile0, nsplit, ws, counters);  \
+    else                                                                                                 \
+      hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX, TAB, false>), dim3(grid), block, 0, stream,   \
+                         a, a_s, b, b_s, c, m, n, k, tiles_m, tiles_n, bias, 0, 1, nullptr, nullptr,     \
+                         counters, zero_n);                                                              \
+  } while (0)
+  // the scale table loads each row's scales in 16-byte pieces; the MX-scaled
+  // kernel reads its exponents from it
+  const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
+  if (c_bf16) {
+    if (tab && a_s_pow2) FP8BSQ_TILE(true, true, true);
+    else if (tab) FP8BSQ_TILE(true, false, true);
+    else FP8BSQ_TILE(true, false, false);
+  } else {
+    if (tab && a_s_pow2) FP8BSQ_TILE(false, true, true);
+    else if (tab) FP8BSQ_TILE(false, false, true);
+    else FP8BSQ_TILE(false, false, false);
+  }
+#undef FP8BSQ_TILE
+  return hipGetLastError();
+}
+
+__global__ void zero_u32_kernel(uint32_t *p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// Split-K plan: when the tiles leave a last round that fills at most half the
+// CUs, those `tail` tiles run in `parts` parts over K (whole scale-table
+// chunks of at least kSplitMinKb K blocks each), `parts` times as many
+// workgroups for 1/parts of the work each.  The full rounds run unsplit.
+constexpr int kSplitMinKb = 16;
+struct SplitPlan {
+  int full = 0, tail = 0, parts = 1;
+  size_t counter_bytes = 0, bytes = 0;   // bytes = 0: no split
+};
+static SplitPlan split_plan(int64_t m, int64_t n, int64_t k) {
+  SplitPlan p;
+  if (!tiled_path(m, n, k)) return p;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return p;
+  const int64_t tiles = ((m + kTileM - 1) / kTileM) * ((n + kTileN - 1) / kTileN);
+  const int full = (int)(tiles / cus * cus), tail = (int)(tiles - full);
+  const int nkb = (int)(k / kBlock), nch = (nkb + kTabKb - 1) / kTabKb;
+  if (tail == 0) return p;
+  int parts = min(min(cus / tail, kSplitMax), min(nch, nkb / kSplitMinKb));
+  if (parts < 2) return p;
+  const int per = (nch + parts - 1) / parts;   // chunks per part, as the kernel divides them
+  parts = (nch + per - 1) / per;               // parts that get any
+  if (parts < 2) return p;
+  p.full = full;
+  p.tail = tail;
+  p.parts = parts;
+  p.counter_bytes = ((size_t)tail * 4 + 255) / 256 * 256;
+  p.bytes = p.counter_bytes + (size_t)tail * parts * kTileM * kTileN * sizeof(float);
+  return p;
+}
+
+size_t block_gemm_split_bytes(int64_t m, int64_t n, int64_t k) { return split_plan(m, n, k).bytes; }
+
+hipError_t launch_block_gemm_split(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                   const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                                   int64_t k, hipStream_t stream, bool a_s_pow2, void *workspace,
+                                   size_t workspace_bytes) {
+  const SplitPlan p = split_plan(m, n, k);
+  if (p.bytes == 0 || workspace_bytes < p.bytes)
+    return launch_block_gemm(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, nullptr, a_s_pow2);
+  uint32_t *counters = (uint32_t *)workspace;
+  float *partials = (float *)((uint8_t *)workspace + p.counter_bytes);
+  // the full rounds, whose workgroup 0 clears the tail's counters; without
+  // full rounds, a one-workgroup fill does
+  if (p.full > 0) {
+    const hipError_t e = launch_tiles(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, nullptr, a_s_pow2,
+                                      (unsigned)p.full, false, 0, 1, nullptr, counters, p.tail);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, counters, p.tail);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_tiles(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, nullptr, a_s_pow2,
+                      (unsigned)(p.tail * p.parts), true, p.full, p.parts, partials, counters);
+}
+
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream, const void *bias, bool a_s_pow2) {
   const bool reference = reference_kernel_forced();
-  // the tiled kernel addresses A, B and a_s with 32-bit per-lane offsets
-  const bool offsets_fit = m * k < ((int64_t)1 << 32) && n * k < ((int64_t)1 << 32);
-  if (!reference && m > 64 && offsets_fit) {
-    const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-#define FP8BSQ_TILE(BF16, MX, TAB)                                                                   \
-  hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX, TAB>), grid, block, 0, stream, a, a_s, b, b_s, c, \
-                     m, n, k, tiles_m, tiles_n, bias)
-    // the scale table loads each row's scales in 16-byte pieces; the MX-scaled
-    // kernel reads its exponents from it
-    const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
-    if (c_bf16) {
-      if (tab && a_s_pow2) FP8BSQ_TILE(true, true, true);
-      else if (tab) FP8BSQ_TILE(true, false, true);
-      else FP8BSQ_TILE(true, false, false);
-    } else {
-      if (tab && a_s_pow2) FP8BSQ_TILE(false, true, true);
-      else if (tab) FP8BSQ_TILE(false, false, true);
-      else FP8BSQ_TILE(false, false, false);
-    }
-#undef FP8BSQ_TILE
-    return hipGetLastError();
+  if (tiled_path(m, n, k)) {
+    const int64_t tiles = ((m + kTileM - 1) / kTileM) * ((n + kTileN - 1) / kTileN);
+    return launch_tiles(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, bias, a_s_pow2, (unsigned)tiles,
+                        false, 0, 1, nullptr, nullptr);
   }
   // the decode kernel's A and weight transfers use 32-bit lane offsets (from A's
   // base, and from each wave's first weight row)

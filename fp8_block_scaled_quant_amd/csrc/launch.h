@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fp8bsq {
@@ -27,6 +28,17 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream, const void *bias = nullptr,
                              bool a_s_pow2 = false);
+
+// launch_block_gemm with split-K for a last round of tiles that would leave
+// CUs idle.  workspace: block_gemm_split_bytes(m, n, k) bytes, 256-byte
+// aligned, whose leading counters are zero on entry and again on completion.
+// With a smaller workspace (or when no split pays), the same launch as
+// launch_block_gemm.
+size_t block_gemm_split_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_block_gemm_split(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                   const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                                   int64_t k, hipStream_t stream, bool a_s_pow2, void *workspace,
+                                   size_t workspace_bytes);
 
 // Fused act_quant + decode GEMM (bf16 x [m, k], m small enough for
 // act_quant_gemm_fusable): C = Q(x) . B^T (+ bias); a_q / a_s receive

@@ -27,6 +27,7 @@
 #ifndef FP8BSQ_H
 #define FP8BSQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #define FP8BSQ_API __attribute__((visibility("default")))
@@ -181,6 +182,46 @@ FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t 
 FP8BSQ_API int fp8_block_gemm_ue8m0(const uint8_t *a, const float *a_s, const uint8_t *b,
                          const float *b_s, void *c, int c_dtype, int64_t m, int64_t n, int64_t k,
                          void *hip_stream);
+
+/*
+ * fp8_block_gemm_split -- fp8_block_gemm / fp8_block_gemm_ue8m0 (scale_fmt
+ * FP8BSQ_SCALE_NONE / FP8BSQ_SCALE_UE8M0) with split-K for a last round of
+ * tiles that would leave compute units idle.
+ *
+ * Same product as fp8_block_gemm (per 128-wide K block, the partial times
+ * a_s * b_s accumulated in FP32; the page "How weight_dequant Handles
+ * Per-Block Scaling in DeepSeek-V3 FP8 GEMM", section "Relationship to FP8
+ * GEMM Operations").  When the 256 x 256 output tiles fill the device's compute
+ * units in whole rounds plus a last round of at most half of them, that last
+ * round's tiles are computed in 2-4 parts over consecutive K ranges, and
+ * their FP32 partial tiles are added in part order (P0 + P1 + ...) before the
+ * output rounding.  Only the summation order differs from fp8_block_gemm, so
+ * results meet the same bound but need not be bit-identical to it.
+ *
+ *   workspace        device memory of fp8_block_gemm_split_workspace(m, n, k)
+ *                    bytes, 256-byte aligned, owned by the caller: scratch
+ *                    for the partial tiles and per-tile counters, with no
+ *                    initial contents required (the call clears the counters
+ *                    itself, in the first of its launches).  Calls in flight
+ *                    at the same time need separate workspaces.
+ *   workspace_bytes  its size.  NULL or a smaller size runs the unsplit launch
+ *                    of fp8_block_gemm (same results up to summation order).
+ *
+ * Other arguments, layouts and errors as for fp8_block_gemm; workspace must be
+ * 256-byte aligned (FP8BSQ_EALIGN).
+ */
+FP8BSQ_API int fp8_block_gemm_split(const uint8_t *a, const float *a_s, const uint8_t *b,
+                         const float *b_s, void *c, int c_dtype, int64_t m, int64_t n, int64_t k,
+                         int scale_fmt, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * fp8_block_gemm_split_workspace -- bytes of workspace fp8_block_gemm_split
+ * uses for an [m, k] x [n, k] product on the current HIP device: 0 when no
+ * split pays for this shape there (the call then needs no workspace), or for
+ * arguments fp8_block_gemm would reject.  Queries the device's compute-unit
+ * count; queues no work.
+ */
+FP8BSQ_API size_t fp8_block_gemm_split_workspace(int64_t m, int64_t n, int64_t k);
 
 /*
  * fp8_act_quant_gemm -- a linear layer's forward product in one call:

@@ -171,3 +171,39 @@ def act_quant_gemm(x: torch.Tensor, b: np.ndarray, b_s: np.ndarray, scale_fmt=No
 
 def announce(msg: str):
     print(f"[gpu-test] {msg}", flush=True)
+
+
+def block_gemm_split(a_dev: torch.Tensor, a_s_dev: torch.Tensor, b: np.ndarray, b_s: np.ndarray,
+                     out: str = "bf16", ue8m0: bool = False, ws: "Guarded" = None, ws_bytes: int = None):
+    """fp8_block_gemm_split with a canary-guarded output and workspace.
+
+    ws_bytes defaults to what fp8_block_gemm_split_workspace asks for; pass
+    ws to reuse a workspace (its contents are left as the last call left
+    them).  Returns (C as float64 numpy, the workspace).
+    """
+    dev = device()
+    m, k = a_dev.shape
+    n = b.shape[0]
+    bd = torch.from_numpy(b).to(dev)
+    bsd = torch.from_numpy(b_s).to(dev)
+    lib = _lib.lib()
+    need = lib.fp8_block_gemm_split_workspace(m, n, k)
+    if ws is None:
+        ws = Guarded(max(need if ws_bytes is None else ws_bytes, 256))
+    nbytes = ws.nbytes if ws_bytes is None else ws_bytes
+    esz = 2 if out == "bf16" else 4
+    c = Guarded(m * n * esz)
+    st = lib.fp8_block_gemm_split(ctypes.c_void_p(a_dev.data_ptr()), ctypes.c_void_p(a_s_dev.data_ptr()),
+                                  ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(bsd.data_ptr()),
+                                  ctypes.c_void_p(c.ptr), _lib.BF16 if out == "bf16" else _lib.F32, m, n, k,
+                                  _lib.SCALE_UE8M0 if ue8m0 else _lib.SCALE_NONE, ctypes.c_void_p(ws.ptr),
+                                  nbytes, stream())
+    assert st == _lib.OK, st
+    torch.cuda.synchronize()
+    c.check_guards()
+    ws.check_guards()
+    raw = c.payload().cpu().numpy()
+    if out == "bf16":
+        bits = raw.view(np.uint16).reshape(m, n).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64), ws
+    return raw.view(np.float32).reshape(m, n).astype(np.float64), ws

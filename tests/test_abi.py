@@ -97,6 +97,21 @@ def test_block_gemm_validation(lib, name):
     assert f(P, P, P, P, P, 1, 1 << 40, 16, 128, None) == _lib.ERANGE
 
 
+def test_block_gemm_split_validation(lib):
+    f = lib.fp8_block_gemm_split
+    assert f(None, P, P, P, P, 1, 16, 16, 128, 0, P, 1024, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, 16, 0, 128, 0, P, 1024, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, 16, 16, 128, 2, P, 1024, None) == _lib.EINVAL      # scale_fmt
+    assert f(P, P, P, P, P, 1, 16, 16, 100, 0, P, 1024, None) == _lib.ESHAPE
+    assert f(P, P, P, P, P, 1, 16, 16, 128, 0, P + 16, 1024, None) == _lib.EALIGN  # workspace
+    assert f(P + 8, P, P, P, P, 1, 16, 16, 128, 1, P, 1024, None) == _lib.EALIGN
+    assert f(P, P, P, P, P, 1, 1 << 40, 16, 128, 0, P, 1024, None) == _lib.ERANGE
+    # sizes the GEMM would reject need no workspace (answered before any HIP call)
+    assert lib.fp8_block_gemm_split_workspace(0, 16, 128) == 0
+    assert lib.fp8_block_gemm_split_workspace(16, 16, 100) == 0
+    assert lib.fp8_block_gemm_split_workspace(1 << 40, 16, 128) == 0
+
+
 def test_weight_quant_validation(lib):
     f = lib.fp8_weight_quant
     assert f(None, 1, 8, 8, 128, 0, P, P, None) == _lib.EINVAL
