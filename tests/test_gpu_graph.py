@@ -1,9 +1,10 @@
 """HIP graph capture of the quantize-and-multiply path.
 
 No entry point allocates, synchronizes or issues a memset (split-K clears
-its counters with a kernel), so a step made of them captures into a graph (torch.cuda.graph): the decode case, where one
-step is ~25 us of kernel time and launch overhead matters, a tiled one, and
-a split-K one (its workspace from torch's graph pool).
+its counters with a kernel), so a step made of them captures into a graph
+(torch.cuda.graph): the decode case, where one step is ~25 us of kernel time
+and launch overhead matters, a tiled one, and a split-K one (its workspace
+from torch's graph pool).
 Each case replays the graph on several fresh inputs copied into the captured
 input buffer, with eager work and synchronizations between replays, and
 checks every replay bit for bit against the same calls made eagerly.
