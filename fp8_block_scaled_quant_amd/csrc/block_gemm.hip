@@ -475,13 +475,19 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // every part from the workspace, this one's included: a select
-        // between acc and a load would pin acc to memory for the whole kernel
-        f32x4 sum = *(const f32x4 *)(base + (i * 8 + j) * 256);
+        // Two parts: own + other, the same either way round (FP32 addition
+        // commutes).  More: every part from the workspace in part order, this
+        // one's included; a select between acc and a loaded value would pin
+        // acc to memory for the whole kernel.
+        if (nsplit == 2) {
+          acc[i][j] += *(const f32x4 *)(base + (size_t)(part ^ 1) * tile_floats + (i * 8 + j) * 256);
+        } else {
+          f32x4 sum = *(const f32x4 *)(base + (i * 8 + j) * 256);
 #pragma unroll
-        for (int p = 1; p < kSplitMax; ++p)
-          if (p < nsplit) sum += *(const f32x4 *)(base + (size_t)p * tile_floats + (i * 8 + j) * 256);
-        acc[i][j] = sum;
+          for (int p = 1; p < kSplitMax; ++p)
+            if (p < nsplit) sum += *(const f32x4 *)(base + (size_t)p * tile_floats + (i * 8 + j) * 256);
+          acc[i][j] = sum;
+        }
       }
   }
 
