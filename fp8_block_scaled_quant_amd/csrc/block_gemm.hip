@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     int tiles_m, int tiles_n, const void *__restrict__ bias, int tile0 = 0, int nsplit = 1,
     float *__restrict__ ws = nullptr, uint32_t *__restrict__ counters = nullptr,
-    uint32_t *__restrict__ zero_ptr = nullptr, int zero_n = 0) {
+    uint32_t *__restrict__ zero_ptr = nullptr, int zero_n = 0, int tile_end = 0) {
   __shared__ __attribute__((aligned(1024))) TileSmem sm;
   if (!kSplit && blockIdx.x == 0)
     for (int i = threadIdx.x; i < zero_n; i += kThreads) zero_ptr[i] = 0u;
@@ -257,252 +257,262 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int nkb = (int)(k / kBlock);
-  int tm, tn, tslot = 0, part = 0, kb_begin = 0, kb_end = nkb;
-  if (kSplit) {
-    // Workgroups are dealt to the 8 XCDs round-robin.  With whole XCD shares
-    // of the tail, workgroup w of XCD w % 8 takes tile 8 u + w % 8 of the
-    // tail (its home XCD in the tile order, next to the tiles it shares A and
-    // B rows with) and part (w / 8) / (tail / 8): that XCD's tiles, part by part.
-    const int ntail = gridDim.x / nsplit;
-    if (ntail % 8 == 0 && tile0 % 8 == 0) {
-      const int local = blockIdx.x / 8, per = ntail / 8;
-      part = local / per;
-      tslot = 8 * (local % per) + blockIdx.x % 8;
+  // Unsplit launches are persistent: one workgroup per CU walks tiles
+  // blockIdx.x, + gridDim.x, ... below tile_end, so a tile's first transfers
+  // go out while the previous tile's output stores drain, with no workgroup
+  // launch in between.  A split launch runs one tile part per workgroup.
+  for (int tile_it = blockIdx.x;; tile_it += gridDim.x) {
+    if (!kSplit && tile_it >= tile_end) break;
+    int tm, tn, tslot = 0, part = 0, kb_begin = 0, kb_end = nkb;
+    if (kSplit) {
+      // Workgroups are dealt to the 8 XCDs round-robin.  With whole XCD shares
+      // of the tail, workgroup w of XCD w % 8 takes tile 8 u + w % 8 of the
+      // tail (its home XCD in the tile order, next to the tiles it shares A and
+      // B rows with) and part (w / 8) / (tail / 8): that XCD's tiles, part by part.
+      const int ntail = gridDim.x / nsplit;
+      if (ntail % 8 == 0 && tile0 % 8 == 0) {
+        const int local = blockIdx.x / 8, per = ntail / 8;
+        part = local / per;
+        tslot = 8 * (local % per) + blockIdx.x % 8;
+      } else {
+        tslot = blockIdx.x / nsplit;
+        part = blockIdx.x % nsplit;
+      }
+      // whole chunks of the scale table per part
+      const int per = ((nkb + kTabKb - 1) / kTabKb + nsplit - 1) / nsplit * kTabKb;
+      kb_begin = min(nkb, part * per);
+      kb_end = min(nkb, kb_begin + per);
+      tile_coords(tile0 + tslot, tiles_m, tiles_n, tm, tn);
     } else {
-      tslot = blockIdx.x / nsplit;
-      part = blockIdx.x % nsplit;
+      tile_coords(tile_it, tiles_m, tiles_n, tm, tn);
     }
-    // whole chunks of the scale table per part
-    const int per = ((nkb + kTabKb - 1) / kTabKb + nsplit - 1) / nsplit * kTabKb;
-    kb_begin = min(nkb, part * per);
-    kb_end = min(nkb, kb_begin + per);
-    tile_coords(tile0 + tslot, tiles_m, tiles_n, tm, tn);
-  } else {
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  }
-  const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
-  const int64_t grid_n = (n + kBlock - 1) / kBlock;
-  const float *bs_row = b_s + min((n0 + wn) / kBlock, grid_n - 1) * nkb;
+    const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
+    const int64_t grid_n = (n + kBlock - 1) / kBlock;
+    const float *bs_row = b_s + min((n0 + wn) / kBlock, grid_n - 1) * nkb;
 
-  // DMA plan, in 8-row groups (one instruction each; lane p of a group fills
-  // slot p: row 8 g + p / 8, chunk slot p % 8): A group 8 d + g (g < 8) by
-  // wave d < 4, B group 4 w + h (h < 4) by every wave w.  Rows past the matrix
-  // edge re-read the last row; their outputs are never stored.
-  const bool dma_wave = wave < 4;
-  const int dw = wave & 3;
-  const int dr = lane >> 3, ds = lane & 7;
-  uint32_t a_off[8], b_off[4];
+    // DMA plan, in 8-row groups (one instruction each; lane p of a group fills
+    // slot p: row 8 g + p / 8, chunk slot p % 8): A group 8 d + g (g < 8) by
+    // wave d < 4, B group 4 w + h (h < 4) by every wave w.  Rows past the matrix
+    // edge re-read the last row; their outputs are never stored.
+    const bool dma_wave = wave < 4;
+    const int dw = wave & 3;
+    const int dr = lane >> 3, ds = lane & 7;
+    uint32_t a_off[8], b_off[4];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int row = 8 * (8 * dw + g) + dr;
-    a_off[g] = (uint32_t)(min(m0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
-  }
+    for (int g = 0; g < 8; ++g) {
+      const int row = 8 * (8 * dw + g) + dr;
+      a_off[g] = (uint32_t)(min(m0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
+    }
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int row = 8 * (4 * wave + h) + dr;
-    b_off[h] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
-  }
-  // scales of the 32-row blocks dw and dw + 4: generic, lanes 0..31 -> rows;
-  // table, lane p -> row p % 32 and K blocks 4 (p / 32) .. +3 of the chunk
-  uint32_t s_off[2];
+    for (int h = 0; h < 4; ++h) {
+      const int row = 8 * (4 * wave + h) + dr;
+      b_off[h] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
+    }
+    // scales of the 32-row blocks dw and dw + 4: generic, lanes 0..31 -> rows;
+    // table, lane p -> row p % 32 and K blocks 4 (p / 32) .. +3 of the chunk
+    uint32_t s_off[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t row = min(m0 + 32 * (dw + 4 * h) + (lane & 31), m - 1);
-    s_off[h] = (uint32_t)(row * nkb * 4 + (kTab ? (lane >> 5) * 16 : 0));
-  }
-  const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]),
-                 lds_s = lds_addr(&sm.as[0][0]);
+    for (int h = 0; h < 2; ++h) {
+      const int64_t row = min(m0 + 32 * (dw + 4 * h) + (lane & 31), m - 1);
+      s_off[h] = (uint32_t)(row * nkb * 4 + (kTab ? (lane >> 5) * 16 : 0));
+    }
+    const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]),
+                   lds_s = lds_addr(&sm.as[0][0]);
 
-  // K block kb's A (and, without the table, its scales) into stage s: waves 0-3
-  auto issue_a = [&](int kb, int s) {
-    const uint8_t *ab = a + (int64_t)kb * kBlock;
+    // K block kb's A (and, without the table, its scales) into stage s: waves 0-3
+    auto issue_a = [&](int kb, int s) {
+      const uint8_t *ab = a + (int64_t)kb * kBlock;
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
-      lds_dma16(ab, a_off[g], lds_a + s * (kTileM * kBlock) + (8 * dw + g) * 1024);
-    if (!kTab) {
+      for (int g = 0; g < 8; ++g)
+        lds_dma16(ab, a_off[g], lds_a + s * (kTileM * kBlock) + (8 * dw + g) * 1024);
+      if (!kTab) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (lane < 32) lds_dma4(a_s + kb, s_off[h], lds_s + s * (kTileM * 4) + 32 * (dw + 4 * h) * 4);
+      }
+    };
+    // K block kb's B into stage s: every wave
+    auto issue_b = [&](int kb, int s) {
+      const uint8_t *bb = b + (int64_t)kb * kBlock;
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        lds_dma16(bb, b_off[h], lds_b + s * (kTileN * kBlock) + (4 * wave + h) * 1024);
+    };
+    // chunk c of the scale table (K blocks kTabKb c ..), into buffer c & 1; in
+    // a last, half-filled chunk the upper lanes re-read their row's first four
+    // scales (in bounds, never used)
+    auto issue_tab = [&](int c) {
+      const int kb0 = kTabKb * c;
+      const bool inside = kb0 + 4 * (lane >> 5) < nkb;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        if (lane < 32) lds_dma4(a_s + kb, s_off[h], lds_s + s * (kTileM * 4) + 32 * (dw + 4 * h) * 4);
-    }
-  };
-  // K block kb's B into stage s: every wave
-  auto issue_b = [&](int kb, int s) {
-    const uint8_t *bb = b + (int64_t)kb * kBlock;
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      lds_dma16(bb, b_off[h], lds_b + s * (kTileN * kBlock) + (4 * wave + h) * 1024);
-  };
-  // chunk c of the scale table (K blocks kTabKb c ..), into buffer c & 1; in
-  // a last, half-filled chunk the upper lanes re-read their row's first four
-  // scales (in bounds, never used)
-  auto issue_tab = [&](int c) {
-    const int kb0 = kTabKb * c;
-    const bool inside = kb0 + 4 * (lane >> 5) < nkb;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      lds_dma16(a_s, inside ? s_off[h] + (uint32_t)kb0 * 4 : s_off[h] - (uint32_t)(lane >> 5) * 16,
-                lds_s + (c & 1) * (kTileM * kTabKb * 4) + (dw + 4 * h) * 1024);
-  };
-
-  const int fr = lane & 15, fq = lane >> 4;
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto step = [&](int kb, int cur) {
-    const float sbv = bs_row[kb];   // scalar load, issued ahead of the wait below
-    wait_dma_all();
-    workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
-    if (dma_wave) {
-      if (kb + 1 < kb_end) issue_a(kb + 1, cur ^ 1);
-      // the table buffer of chunk c + 1 was last read in chunk c - 1
-      if (kTab && kb % kTabKb == 0 && kb + kTabKb < kb_end) issue_tab(kb / kTabKb + 1);
-    }
-    // Retire the scalar load now (the empty asm consumes its value): scalar and
-    // LDS results share one counter and the scalar one may return out of order,
-    // so while it is outstanding every LDS wait would have to be a full drain.
-    asm volatile("" ::"s"(sbv));
-    // fragment reads first: the first MFMA waits only for these
-    i32x8 af[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm + 16 * i + fr;
-      af[i] = frag_from_lds(&sm.a[cur][r * kBlock], fq, r);
-    }
-    auto read_b = [&](int j) {
-      const int r = wn + 16 * j + fr;
-      return frag_from_lds(&sm.b[cur][r * kBlock], fq, r);
+        lds_dma16(a_s, inside ? s_off[h] + (uint32_t)kb0 * 4 : s_off[h] - (uint32_t)(lane >> 5) * 16,
+                  lds_s + (c & 1) * (kTileM * kTabKb * 4) + (dw + 4 * h) * 1024);
     };
-    i32x8 bcur = read_b(0), bnext;
-    // kMxA (activation scales that are powers of two, act_quant's ue8m0): the
-    // MFMA applies a_s of the A row a lane feeds (its E8M0 exponent, the fp32
-    // exponent field), leaving the rescale a multiply by the wave-uniform b_s.
-    // P * 2^e is exact, so fma(P * a_s, b_s, acc) equals the generic
-    // fma(P, a_s * b_s, acc) bit for bit.
-    f32x4 sav[4];
-    int ea[4];
-    const float *tab = &sm.tab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
-    // table row r = wm + 16 i + x lies in 32-row block wm / 32 + i / 2, at row
-    // 16 (i % 2) + x of it; the MFMA scale wants x = fr, the rescale x = 4 fq + e
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float *tb = tab + (wm / 32 + i / 2) * 256 + 16 * (i % 2) * 4;
-      if (kMxA) {
-        ea[i] = (int)((__float_as_uint(tb[fr * 4]) >> 23) & 0xFFu);
-      } else if (kTab) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sav[i][e] = tb[(4 * fq + e) * 4];
-      } else {
-        sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
-      }
-    }
-    // MFMA q = 4 j + i; its rescale runs three MFMAs later (ring of 4 partials).
-    // The row scales a_s * b_s are formed at their first use (q - 3 < 4), so
-    // their LDS reads never hold up the first MFMAs.
-    float sc[4][4];
-    f32x4 part[4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j + 1 < 8) bnext = read_b(j + 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = 4 * j + i;
-        part[q % 4] = kMxA ? mfma_e4m3_16x16x128_mx(af[i], bcur, ea[i])
-                           : mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
-        // the next block's B, unconditionally so that no branch splits the
-        // unrolled loop (the last block re-reads itself into the stage no one
-        // reads again; drained after the loop)
-        if (j == 2 && i == 0) issue_b(min(kb + 1, kb_end - 1), cur ^ 1);
-        if (q >= 3) {
-          const int qp = q - 3, ip = qp % 4, jp = qp / 4;
-          if (!kMxA && qp < 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sc[ip][e] = sav[ip][e] * sbv;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (j + 1 < 8) bcur = bnext;
-    }
-#pragma unroll
-    for (int qp = 29; qp < 32; ++qp) {
-      const int ip = qp % 4, jp = qp / 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
-    }
-  };
 
-  if (dma_wave) {
-    issue_a(kb_begin, 0);
-    if (kTab) issue_tab(kb_begin / kTabKb);
-  }
-  issue_b(kb_begin, 0);
-#pragma nounroll
-  for (int kb = kb_begin; kb < kb_end; ++kb) step(kb, (kb - kb_begin) & 1);
-  wait_dma_all();
-
-  if (kSplit) {
-    // partials in the lanes' own order: [tile][part][wave][i][j][lane][4]
-    const size_t tile_floats = (size_t)kTileM * kTileN;
-    float *base = ws + (size_t)tslot * nsplit * tile_floats + (size_t)wave * (tile_floats / 8) + lane * 4;
-    float *mine = base + (size_t)part * tile_floats;
+    const int fr = lane & 15, fq = lane >> 4;
+    f32x4 acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) *(f32x4 *)(mine + (i * 8 + j) * 256) = acc[i][j];
-    // Every wave's stores complete (in L2) before the barrier; one device-scope
-    // fence then publishes the workgroup's partial ahead of its count, and the
-    // last part's fence makes the others' partials visible before it reads
-    // them.  (Each fence writes back or invalidates a whole L2, so one per
-    // workgroup, not one per thread.)
-    wait_dma_all();
-    __syncthreads();
-    if (t == 0) {
-      __threadfence();
-      split_last = atomicAdd(&counters[tslot], 1u) == (uint32_t)(nsplit - 1);
-      if (split_last) __threadfence();
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int kb, int cur) {
+      const float sbv = bs_row[kb];   // scalar load, issued ahead of the wait below
+      wait_dma_all();
+      workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
+      if (dma_wave) {
+        if (kb + 1 < kb_end) issue_a(kb + 1, cur ^ 1);
+        // the table buffer of chunk c + 1 was last read in chunk c - 1
+        if (kTab && kb % kTabKb == 0 && kb + kTabKb < kb_end) issue_tab(kb / kTabKb + 1);
+      }
+      // Retire the scalar load now (the empty asm consumes its value): scalar and
+      // LDS results share one counter and the scalar one may return out of order,
+      // so while it is outstanding every LDS wait would have to be a full drain.
+      asm volatile("" ::"s"(sbv));
+      // fragment reads first: the first MFMA waits only for these
+      i32x8 af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm + 16 * i + fr;
+        af[i] = frag_from_lds(&sm.a[cur][r * kBlock], fq, r);
+      }
+      auto read_b = [&](int j) {
+        const int r = wn + 16 * j + fr;
+        return frag_from_lds(&sm.b[cur][r * kBlock], fq, r);
+      };
+      i32x8 bcur = read_b(0), bnext;
+      // kMxA (activation scales that are powers of two, act_quant's ue8m0): the
+      // MFMA applies a_s of the A row a lane feeds (its E8M0 exponent, the fp32
+      // exponent field), leaving the rescale a multiply by the wave-uniform b_s.
+      // P * 2^e is exact, so fma(P * a_s, b_s, acc) equals the generic
+      // fma(P, a_s * b_s, acc) bit for bit.
+      f32x4 sav[4];
+      int ea[4];
+      const float *tab = &sm.tab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
+      // table row r = wm + 16 i + x lies in 32-row block wm / 32 + i / 2, at row
+      // 16 (i % 2) + x of it; the MFMA scale wants x = fr, the rescale x = 4 fq + e
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float *tb = tab + (wm / 32 + i / 2) * 256 + 16 * (i % 2) * 4;
+        if (kMxA) {
+          ea[i] = (int)((__float_as_uint(tb[fr * 4]) >> 23) & 0xFFu);
+        } else if (kTab) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sav[i][e] = tb[(4 * fq + e) * 4];
+        } else {
+          sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+        }
+      }
+      // MFMA q = 4 j + i; its rescale runs three MFMAs later (ring of 4 partials).
+      // The row scales a_s * b_s are formed at their first use (q - 3 < 4), so
+      // their LDS reads never hold up the first MFMAs.
+      float sc[4][4];
+      f32x4 part[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j + 1 < 8) bnext = read_b(j + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = 4 * j + i;
+          part[q % 4] = kMxA ? mfma_e4m3_16x16x128_mx(af[i], bcur, ea[i])
+                             : mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
+          // the next block's B, unconditionally so that no branch splits the
+          // unrolled loop (the last block re-reads itself into the stage no one
+          // reads again; drained after the loop)
+          if (j == 2 && i == 0) issue_b(min(kb + 1, kb_end - 1), cur ^ 1);
+          if (q >= 3) {
+            const int qp = q - 3, ip = qp % 4, jp = qp / 4;
+            if (!kMxA && qp < 4) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sc[ip][e] = sav[ip][e] * sbv;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (j + 1 < 8) bcur = bnext;
+      }
+#pragma unroll
+      for (int qp = 29; qp < 32; ++qp) {
+        const int ip = qp % 4, jp = qp / 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
+      }
+    };
+
+    if (dma_wave) {
+      issue_a(kb_begin, 0);
+      if (kTab) issue_tab(kb_begin / kTabKb);
     }
-    __syncthreads();
-    if (!split_last) return;
+    issue_b(kb_begin, 0);
+#pragma nounroll
+    for (int kb = kb_begin; kb < kb_end; ++kb) step(kb, (kb - kb_begin) & 1);
+    wait_dma_all();
+
+    if (kSplit) {
+      // partials in the lanes' own order: [tile][part][wave][i][j][lane][4]
+      const size_t tile_floats = (size_t)kTileM * kTileN;
+      float *base = ws + (size_t)tslot * nsplit * tile_floats + (size_t)wave * (tile_floats / 8) + lane * 4;
+      float *mine = base + (size_t)part * tile_floats;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *(f32x4 *)(mine + (i * 8 + j) * 256) = acc[i][j];
+      // Every wave's stores complete (in L2) before the barrier; one device-scope
+      // fence then publishes the workgroup's partial ahead of its count, and the
+      // last part's fence makes the others' partials visible before it reads
+      // them.  (Each fence writes back or invalidates a whole L2, so one per
+      // workgroup, not one per thread.)
+      wait_dma_all();
+      __syncthreads();
+      if (t == 0) {
+        __threadfence();
+        split_last = atomicAdd(&counters[tslot], 1u) == (uint32_t)(nsplit - 1);
+        if (split_last) __threadfence();
+      }
+      __syncthreads();
+      if (!split_last) return;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // Two parts: own + other, the same either way round (FP32 addition
+          // commutes).  More: every part from the workspace in part order, this
+          // one's included; a select between acc and a loaded value would pin
+          // acc to memory for the whole kernel.
+          if (nsplit == 2) {
+            acc[i][j] += *(const f32x4 *)(base + (size_t)(part ^ 1) * tile_floats + (i * 8 + j) * 256);
+          } else {
+            f32x4 sum = *(const f32x4 *)(base + (i * 8 + j) * 256);
+#pragma unroll
+            for (int p = 1; p < kSplitMax; ++p)
+              if (p < nsplit) sum += *(const f32x4 *)(base + (size_t)p * tile_floats + (i * 8 + j) * 256);
+            acc[i][j] = sum;
+          }
+        }
+    }
+
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // Two parts: own + other, the same either way round (FP32 addition
-        // commutes).  More: every part from the workspace in part order, this
-        // one's included; a select between acc and a loaded value would pin
-        // acc to memory for the whole kernel.
-        if (nsplit == 2) {
-          acc[i][j] += *(const f32x4 *)(base + (size_t)(part ^ 1) * tile_floats + (i * 8 + j) * 256);
-        } else {
-          f32x4 sum = *(const f32x4 *)(base + (i * 8 + j) * 256);
+        const int64_t col = n0 + wn + 16 * j + fr;
+        const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
 #pragma unroll
-          for (int p = 1; p < kSplitMax; ++p)
-            if (p < nsplit) sum += *(const f32x4 *)(base + (size_t)p * tile_floats + (i * 8 + j) * 256);
-          acc[i][j] = sum;
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = m0 + wm + 16 * i + 4 * fq + e;
+          if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][e] + bv);
         }
       }
+    if (kSplit) break;
+    // every wave is done with this tile's LDS before the next tile's first transfers
+    workgroup_barrier();
   }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t col = n0 + wn + 16 * j + fr;
-      const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm + 16 * i + 4 * fq + e;
-        if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][e] + bv);
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -882,8 +892,9 @@ static bool tiled_path(int64_t m, int64_t n, int64_t k) {
          n * k < ((int64_t)1 << 32);
 }
 
-// Tiled kernel over `grid` workgroups (see block_gemm_tile_kernel for tile0,
-// nsplit, ws and counters; split selects the split-K instantiation).
+// Tiled kernel: unsplit, tiles [0, grid) by min(grid, CUs) persistent
+// workgroups; split, `grid` workgroups (see block_gemm_tile_kernel for tile0,
+// nsplit, ws and counters).
 static hipError_t launch_tiles(const uint8_t *a, const float *a_s, const uint8_t *b,
                                const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream, const void *bias, bool a_s_pow2,
@@ -891,15 +902,20 @@ static hipError_t launch_tiles(const uint8_t *a, const float *a_s, const uint8_t
                                uint32_t *counters, int zero_n = 0) {
   const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
   const dim3 block(kThreads);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const unsigned pgrid = grid < (unsigned)cus ? grid : (unsigned)cus;
 #define FP8BSQ_TILE(BF16, MX, TAB)                                                                      \
   do {                                                                                                   \
     if (split)                                                                                           \
       hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX, TAB, true>), dim3(grid), block, 0, stream, a, \
                          a_s, b, b_s, c, m, n, k, tiles_m, tiles_n, bias, tile0, nsplit, ws, counters);  \
     else                                                                                                 \
-      hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX, TAB, false>), dim3(grid), block, 0, stream,   \
+      hipLaunchKernelGGL((block_gemm_tile_kernel<BF16, MX, TAB, false>), dim3(pgrid), block, 0, stream,  \
                          a, a_s, b, b_s, c, m, n, k, tiles_m, tiles_n, bias, 0, 1, nullptr, nullptr,     \
-                         counters, zero_n);                                                              \
+                         counters, zero_n, (int)grid);                                                   \
   } while (0)
   // the scale table loads each row's scales in 16-byte pieces; the MX-scaled
   // kernel reads its exponents from it
