@@ -258,9 +258,10 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int nkb = (int)(k / kBlock);
   // Unsplit launches are persistent: one workgroup per CU walks tiles
-  // blockIdx.x, + gridDim.x, ... below tile_end, so a tile's first transfers
-  // go out while the previous tile's output stores drain, with no workgroup
+  // blockIdx.x, + gridDim.x, ... below tile_end, and issues a tile's first
+  // transfers before the previous tile's output stores, with no workgroup
   // launch in between.  A split launch runs one tile part per workgroup.
+  bool prologue_done = false;
   for (int tile_it = blockIdx.x;; tile_it += gridDim.x) {
     if (!kSplit && tile_it >= tile_end) break;
     int tm, tn, tslot = 0, part = 0, kb_begin = 0, kb_end = nkb;
@@ -298,25 +299,27 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
     const bool dma_wave = wave < 4;
     const int dw = wave & 3;
     const int dr = lane >> 3, ds = lane & 7;
-    uint32_t a_off[8], b_off[4];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int row = 8 * (8 * dw + g) + dr;
-      a_off[g] = (uint32_t)(min(m0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int row = 8 * (4 * wave + h) + dr;
-      b_off[h] = (uint32_t)(min(n0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
-    }
+    uint32_t a_off[8], b_off[4], s_off[2];
     // scales of the 32-row blocks dw and dw + 4: generic, lanes 0..31 -> rows;
     // table, lane p -> row p % 32 and K blocks 4 (p / 32) .. +3 of the chunk
-    uint32_t s_off[2];
+    auto set_offsets = [&](int64_t tm0, int64_t tn0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t row = min(m0 + 32 * (dw + 4 * h) + (lane & 31), m - 1);
-      s_off[h] = (uint32_t)(row * nkb * 4 + (kTab ? (lane >> 5) * 16 : 0));
-    }
+      for (int g = 0; g < 8; ++g) {
+        const int row = 8 * (8 * dw + g) + dr;
+        a_off[g] = (uint32_t)(min(tm0 + row, m - 1) * k + ((ds ^ swz(row)) << 4));
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int row = 8 * (4 * wave + h) + dr;
+        b_off[h] = (uint32_t)(min(tn0 + row, n - 1) * k + ((ds ^ swz(row)) << 4));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t row = min(tm0 + 32 * (dw + 4 * h) + (lane & 31), m - 1);
+        s_off[h] = (uint32_t)(row * nkb * 4 + (kTab ? (lane >> 5) * 16 : 0));
+      }
+    };
+    set_offsets(m0, n0);
     const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]),
                    lds_s = lds_addr(&sm.as[0][0]);
 
@@ -445,14 +448,32 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       }
     };
 
-    if (dma_wave) {
-      issue_a(kb_begin, 0);
-      if (kTab) issue_tab(kb_begin / kTabKb);
+    if (!prologue_done) {
+      if (dma_wave) {
+        issue_a(kb_begin, 0);
+        if (kTab) issue_tab(kb_begin / kTabKb);
+      }
+      issue_b(kb_begin, 0);
     }
-    issue_b(kb_begin, 0);
 #pragma nounroll
     for (int kb = kb_begin; kb < kb_end; ++kb) step(kb, (kb - kb_begin) & 1);
     wait_dma_all();
+
+    // persistent: the next tile's first transfers (stage 0, table chunk 0) go
+    // out before this tile's output stores, once every wave is done with LDS
+    prologue_done = false;
+    if (!kSplit && tile_it + (int)gridDim.x < tile_end) {
+      workgroup_barrier();
+      int ntm, ntn;
+      tile_coords(tile_it + gridDim.x, tiles_m, tiles_n, ntm, ntn);
+      set_offsets((int64_t)ntm * kTileM, (int64_t)ntn * kTileN);
+      if (dma_wave) {
+        issue_a(0, 0);
+        if (kTab) issue_tab(0);
+      }
+      issue_b(0, 0);
+      prologue_done = true;
+    }
 
     if (kSplit) {
       // partials in the lanes' own order: [tile][part][wave][i][j][lane][4]
@@ -509,9 +530,7 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
           if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[i][j][e] + bv);
         }
       }
-    if (kSplit) break;
-    // every wave is done with this tile's LDS before the next tile's first transfers
-    workgroup_barrier();
+    if (kSplit || !prologue_done) break;
   }
 }
 
