@@ -175,6 +175,10 @@ __global__ __launch_bounds__(256) void block_gemm_simple_kernel(
 // Tile order is XCD-aware: workgroup ids are dealt round-robin to the eight
 // XCDs, so consecutive tiles of the grouped raster order (4 M tiles by the N
 // tiles) go to ids of the same XCD and share its L2.
+//
+// Launches: one persistent workgroup per CU walks the tiles; with
+// launch_block_gemm_split a last round of tiles that would leave CUs idle
+// runs in a second launch, split over K (kSplit).
 // ---------------------------------------------------------------------------
 constexpr int kTileM = 256, kTileN = 256, kThreads = 512;
 
