@@ -61,12 +61,16 @@ def _check(got, an, asn, w, ws, rows, out):
 
 # (m, n, k, out, scale_fmt): 272 tiles = 256 + a tail of 16 (on 256 CUs) in
 # 4 parts (K = 8192), 3 parts (K = 6144; ragged and K/128 = 50, no scale
-# table, K = 6400); 8 tiles and no full round (K = 8192, 4 parts)
+# table, K = 6400); 8 tiles and no full round (K = 8192, 4 parts); a tail of
+# 5 (261 tiles: not whole XCD shares, the plain tile-by-part mapping); K/128 =
+# 45, two uneven parts (24 and 21 K blocks) without the scale table
 @pytest.mark.parametrize("m,n,k,out,scale_fmt", [
     (4096, 4352, 8192, "bf16", "ue8m0"),
     (4096, 4352, 6144, "f32", None),
     (4000, 4300, 6400, "bf16", None),
     (512, 1024, 8192, "f32", "ue8m0"),
+    (2304, 7424, 4096, "bf16", "ue8m0"),
+    (4096, 4352, 5760, "bf16", "ue8m0"),
 ])
 def test_split_matches_oracle(m, n, k, out, scale_fmt):
     d = gen.custom_gemm(seed=m + n + k, m=m, n=n, k=k, outliers=True)
