@@ -557,8 +557,9 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 //
 // Fused act_quant (kFuseQ, M <= kFusedMaxM, bf16 activations): every
 // workgroup quantizes all of x [m, k] into LDS in its prologue with
-// act_quant's arithmetic, and workgroup 0 also publishes the codes and
-// scales; there is no mover and no per-block barrier.  The compute waves do
+// act_quant's arithmetic (four blocks' loads in flight per lane), and
+// workgroup 0 also publishes the codes and scales; there is no mover and no
+// per-block barrier.  The compute waves do
 // the same arithmetic in the same order as on the two-call path, so both give
 // bit-identical outputs.
 // ---------------------------------------------------------------------------
@@ -576,32 +577,44 @@ constexpr int kFusedMaxM = 2;
 // each, amax over the 16-lane row, the same scale and quotient arithmetic --
 // into LDS codes aq [m][k] and scales as_t [kb][row].  Workgroup 0 also writes
 // the codes and scales to a_q / a_s_out, bit-identical to fp8_act_quant.
-template <int kRows, int kThreadsQ>
+template <int kRows, int kThreadsQ, int kBatchQ = 4>
 __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int m, int nkb,
                                                 bool ue8m0, uint8_t *aq, float (*as_t)[kRows],
                                                 uint8_t *__restrict__ a_q,
                                                 float *__restrict__ a_s_out, bool publish) {
   const int t = threadIdx.x, row16 = t >> 4, sub = t & 15;
   const int nblocks = m * nkb;                     // blocks of the flat [m * nkb, 128] sequence
-  // the sixteen lanes of a block share its loop trip count, as the row
-  // reduction needs
-  for (int blk = row16; blk < nblocks; blk += kThreadsQ / 16) {
-    const u32x4 v = x[(int64_t)blk * 16 + sub];
-    u16x2 m2 = {0, 0};
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  constexpr int kStride = kThreadsQ / 16;
+  // kBatchQ loads in flight per lane, then their blocks: one load latency per
+  // kBatchQ blocks instead of per block.  The sixteen lanes of a block share
+  // every condition below, as the row reduction needs.
+  for (int base = row16; base < nblocks; base += kBatchQ * kStride) {
+    u32x4 v[kBatchQ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
-    const uint32_t amax = row_max_u32((uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16);
-    float sc, r;
-    block_scale_fast(amax, ue8m0, sc, r);
-    const u32x2 codes = encode_chunk_bf16(v, sc, r);
-    *(u32x2 *)(aq + (int64_t)blk * kBlock + 8 * sub) = codes;
-    const int row = blk / nkb, kb = blk % nkb;
-    if (sub == 0) as_t[kb][row] = sc;
-    if (publish) {
-      *(u32x2 *)(a_q + (int64_t)blk * kBlock + 8 * sub) = codes;
-      if (sub == 0) a_s_out[blk] = sc;
+    for (int u = 0; u < kBatchQ; ++u) {
+      const int blk = base + u * kStride;
+      if (blk < nblocks) v[u] = x[(int64_t)blk * 16 + sub];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatchQ; ++u) {
+      const int blk = base + u * kStride;
+      if (blk >= nblocks) break;
+      u16x2 m2 = {0, 0};
+      const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, d[j] & 0x7FFF7FFFu));
+      const uint32_t amax = row_max_u32((uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16);
+      float sc, r;
+      block_scale_fast(amax, ue8m0, sc, r);
+      const u32x2 codes = encode_chunk_bf16(v[u], sc, r);
+      *(u32x2 *)(aq + (int64_t)blk * kBlock + 8 * sub) = codes;
+      const int row = blk / nkb, kb = blk % nkb;
+      if (sub == 0) as_t[kb][row] = sc;
+      if (publish) {
+        *(u32x2 *)(a_q + (int64_t)blk * kBlock + 8 * sub) = codes;
+        if (sub == 0) a_s_out[blk] = sc;
+      }
     }
   }
 }
