@@ -57,7 +57,10 @@ def test_ue8m0_and_fp32_out(m):
     _run(d["x"], d["w"], d["w_s"], "ue8m0", "f32", "ue8m0/f32")
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 129, 128), (4, 17, 256), (2, 7168, 18432), (7, 500, 640)])
+# fused (bf16, m <= 2): one K block (k = 128) and three; a last batch of four
+# loads per lane that is only partly used (k = 18432: 288 blocks for 80 lanes x 4)
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 129, 128), (4, 17, 256), (2, 7168, 18432), (7, 500, 640),
+                                   (1, 129, 128), (2, 96, 384)])
 def test_shapes(m, n, k):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
     _run(d["x"], d["w"], d["w_s"], None, "bf16", "shape")
