@@ -59,7 +59,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--cpu-rows", type=int, default=4096,
+    p.add_argument("--cpu-rows", type=int, default=6144,
                    help="activation rows in the CPU oracle sample (0 skips it)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--profile-workload", default=None,
