@@ -14,8 +14,10 @@ One step = one pass of the whole path over the prefill-shaped linear layer:
 
 ``value`` = 2*M*N*K / step time (TFLOP/s of the whole step, inputs resident
 in HBM).  Per-kernel times come from HIP events recorded on the stream the
-kernels run on; the GEMM is the dominant kernel and its roofline is the dense
-FP8 MFMA peak.  Each step touches about 1 GB, well beyond the 256 MB Infinity
+kernels run on, created without the system-scope fence a default event adds
+(that fence's cache write-back would otherwise be timed with the next
+kernel); the GEMM is the dominant kernel and its roofline is the dense FP8
+MFMA peak.  Each step touches about 1 GB, well beyond the 256 MB Infinity
 Cache, so every kernel reads its inputs from HBM.
 
 ``cpu_baseline`` times the CPU oracle (test infrastructure, never tuned) on a
@@ -160,6 +162,48 @@ def calibrate_copy():
     print("copied 1073741824 bytes", flush=True)
 
 
+class TimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence.
+
+    A default event performs a system-scope fence (an L2 write-back and
+    invalidate) when it is reached, and a kernel bracketed by such events is
+    timed with that flush and its aftermath.  These events skip it; their
+    elapsed times are read after a device synchronization.  The HIP runtime is
+    the one torch and the library already loaded (soname libamdhip64.so.7).
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, count):
+        import ctypes
+        self._c = ctypes
+        self._hip = hip = ctypes.CDLL("libamdhip64.so.7")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.events.append(e)
+
+    def record(self, i, stream):
+        if self._hip.hipEventRecord(self.events[i], self._c.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i, j):
+        ms = self._c.c_float()
+        if self._hip.hipEventElapsedTime(self._c.byref(ms), self.events[i], self.events[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self._hip.hipEventDestroy(e)
+        self.events = []
+
+
 def cpu_baseline(x_bf16, w, ws, rows):
     """Time the oracle on the first `rows` rows (and rows/M of the weight)."""
     import numpy as np
@@ -219,18 +263,18 @@ def main():
     ws = torch.from_numpy(ws_np).to(dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(i=None):
+        if i is not None:
+            ev.record(4 * i, stream)
         y, s = fb.act_quant(x, 128, "ue8m0")
-        if ev is not None:
-            ev[1].record(stream)
+        if i is not None:
+            ev.record(4 * i + 1, stream)
         wd = fb.weight_dequant(w, ws, 128, torch.bfloat16)
-        if ev is not None:
-            ev[2].record(stream)
+        if i is not None:
+            ev.record(4 * i + 2, stream)
         c = fb.fp8_gemm(y, s, w, ws, torch.bfloat16, "ue8m0")
-        if ev is not None:
-            ev[3].record(stream)
+        if i is not None:
+            ev.record(4 * i + 3, stream)
         return c, wd
 
     for _ in range(args.warmup):
@@ -238,17 +282,18 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronized on both sides
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = TimingEvents(4 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    aq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    dq_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    aq_ms = float(np.mean([ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.steps)]))
+    dq_ms = float(np.mean([ev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]))
+    gm_ms = float(np.mean([ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
+    ev.close()
     ms_per_step = elapsed * 1e3 / args.steps
 
     gemm_tflops = GEMM_FLOP / (gm_ms * 1e-3) / 1e12
