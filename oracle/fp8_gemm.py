@@ -95,11 +95,20 @@ def gemm_tolerance(a, a_s, b, b_s, block_size: int = 128, rows=None, rel: float 
 
 
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
-    """One bf16 ulp at the magnitude of v (float64)."""
+    """One bf16 ulp at the magnitude of v (float64): the spacing of bf16 values
+    in the binade holding |v|.
+
+    bf16 keeps 8 significant bits, so in the binade [2^e, 2^(e+1)) the spacing
+    is 2^(e - 7); below the smallest normal 2^-126 (and at zero) it is the
+    subnormal spacing 2^-133.  The exponent e = floor(log2 |v|) is taken from
+    frexp (|v| = f * 2^E with f in [0.5, 1), so e = E - 1), which is exact for
+    every float64; a rounded log2 is not, just below a power of two.
+    """
     a = np.abs(np.asarray(v, dtype=np.float64))
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.maximum(np.where(a > 0, e, -126.0), -126.0)
-    return np.ldexp(1.0, (e - 7).astype(np.int64))
+    _, big_e = np.frexp(a)
+    e = np.where(a > 0, big_e.astype(np.int64) - 1, -126)
+    e = np.maximum(e, -126)
+    return np.ldexp(1.0, e - 7)
 
 
 def gemm_check(gpu: np.ndarray, c: np.ndarray, tol: np.ndarray, out: str = "f32") -> np.ndarray:

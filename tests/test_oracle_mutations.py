@@ -310,3 +310,74 @@ def test_wq_variant_harness_is_faithful():
 ])
 def test_weight_quant_mutants_caught(name, mutant):
     assert _wq_any_fails(mutant), name
+
+
+# --------------------------------------------------------------- bf16 bound
+
+from tests import test_oracle_bf16 as T_bf  # noqa: E402
+
+gemm_mod = importlib.import_module("oracle.fp8_gemm")
+
+
+def _bf16_bound_any_fails():
+    checks = [
+        (T_bf.check_ulp_spacing, (gemm_mod.bf16_ulp,)),
+        (T_bf.check_ulp_special, (gemm_mod.bf16_ulp,)),
+        (T_bf.check_gemm_bound_bf16, (oracle.gemm_check,)),
+        (T_bf.check_ulp_taken_at_c, (oracle.gemm_check,)),
+    ]
+    return any(_fails(f, *a) for f, a in checks)
+
+
+def _ulp_with(exp_shift=7, floor=-126, log2=False):
+    """bf16_ulp with one step replaced."""
+    def ulp(v):
+        a = np.abs(np.asarray(v, dtype=np.float64))
+        if log2:   # exponent from a rounded log2
+            e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+        else:
+            e = np.frexp(a)[1].astype(np.int64) - 1
+        e = np.maximum(np.where(a > 0, e, floor), floor)
+        return np.ldexp(1.0, e - exp_shift)
+    return ulp
+
+
+def test_bf16_ulp_variant_harness_is_faithful():
+    v = np.concatenate([np.ldexp(1.0, np.arange(-140, 130)), [0.0, 3.0, -5.5, 1e-45]])
+    assert np.array_equal(_ulp_with()(v), gemm_mod.bf16_ulp(v))
+
+
+@pytest.mark.parametrize("name, mutant", [
+    ("two ulps (e - 6)", _ulp_with(exp_shift=6)),
+    ("half an ulp (e - 8)", _ulp_with(exp_shift=8)),
+    ("exponent from a rounded log2", _ulp_with(log2=True)),
+    ("fp32 subnormal floor instead of bf16's", _ulp_with(floor=-149)),
+    ("no subnormal floor at the normal boundary", _ulp_with(floor=-127)),
+])
+def test_bf16_ulp_mutants_caught(name, mutant, monkeypatch):
+    monkeypatch.setattr(gemm_mod, "bf16_ulp", mutant)
+    assert _bf16_bound_any_fails(), name
+
+
+def test_gemm_check_ulp_of_gpu_value_caught():
+    def mutant(gpu, c, tol, out="f32"):
+        gpu = np.asarray(gpu, dtype=np.float64)
+        bound = tol + (gemm_mod.bf16_ulp(gpu) if out == "bf16" else 0.0)
+        return np.isfinite(gpu) & (np.abs(gpu - c) <= bound)
+    assert _fails(T_bf.check_ulp_taken_at_c, mutant)
+
+
+def test_gemm_check_ignores_ulp_caught():
+    def mutant(gpu, c, tol, out="f32"):
+        gpu = np.asarray(gpu, dtype=np.float64)
+        return np.isfinite(gpu) & (np.abs(gpu - c) <= tol)
+    assert _fails(T_bf.check_gemm_bound_bf16, mutant)
+
+
+@pytest.mark.parametrize("name, mutant", [
+    ("sign bit dropped", lambda b: ((np.asarray(b, np.uint16).astype(np.uint32) & 0x7FFF) << 16).view(np.float32)),
+    ("shifted by 15", lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 15).view(np.float32)),
+    ("bytes swapped", lambda b: (np.asarray(b, np.uint16).byteswap().astype(np.uint32) << 16).view(np.float32)),
+])
+def test_bf16_bits_to_f32_mutants_caught(name, mutant):
+    assert _fails(T_bf.check_bits_to_f32, mutant), name
