@@ -1,16 +1,16 @@
 """Throughput of the block-scaled FP8 hot path on one MI355X.
 
-One step = one pass of the whole path over the prefill-shaped linear layer:
+One step = one pass of the whole hot path over the prefill-shaped workload:
 
   1. act_quant (ue8m0 scales) of bf16 activations [8192, 7168]
-     (the act_quant bandwidth workload's shape, 0.1% outliers x100);
-  2. weight_dequant of the E4M3 weight [18432, 7168] with its [144, 56]
-     block scales to bf16 (the dequant bandwidth workload);
-  3. the block-scaled GEMM of the quantized activations with that weight,
-     bf16 out (the prefill GEMM, 8192 x 18432 x 7168), through
-     fp8_block_gemm_ue8m0: the activation scales are act_quant's ue8m0 powers
-     of two, applied inside the MX-scaled MFMA (bit-identical to
-     fp8_block_gemm).
+     (0.1% outliers x100);
+  2. weight_dequant of the E4M3 weight [18432, 7168] with its [144, 56] block
+     scales to bf16 (the dequantizer's step of the path; the GEMM below does
+     not read its output, since it applies the block scales itself);
+  3. the block-scaled GEMM of the quantized activations with that weight, bf16
+     out (8192 x 18432 x 7168), through fp8_block_gemm_ue8m0: the activation
+     scales are act_quant's ue8m0 powers of two, applied inside the MX-scaled
+     MFMA (bit-identical to fp8_block_gemm).
 
 ``value`` = 2*M*N*K / step time (TFLOP/s of the whole step, inputs resident
 in HBM).  Per-kernel times come from HIP events recorded on the stream the
@@ -20,10 +20,18 @@ kernel); the GEMM is the dominant kernel and its roofline is the dense FP8
 MFMA peak.  Each step touches about 1 GB, well beyond the 256 MB Infinity
 Cache, so every kernel reads its inputs from HBM.
 
+``configs`` times every workload on its own, each next to the CPU oracle run
+on the same inputs in this process (the whole tensor where that takes seconds,
+a stated row sample for the prefill GEMMs).  Bandwidth-bound workloads cycle
+through enough copies of their buffers (at least 1 GB in all) that no launch
+finds its inputs in the Infinity Cache.
+
 ``cpu_baseline`` times the CPU oracle (test infrastructure, never tuned) on a
-bounded sample of the same workload: the first ``--cpu-rows`` activation rows
+bounded sample of the step's workload: the first ``--cpu-rows`` activation rows
 through act_quant and the GEMM, and the matching fraction of the weight through
-weight_dequant.
+weight_dequant.  OPENBLAS_NUM_THREADS is set to the host threads this process
+may use before numpy is imported; the thread count, numpy and OpenBLAS versions
+are recorded.
 
 ``roofline.traffic`` is the GEMM's HBM traffic per launch measured with
 rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
@@ -31,7 +39,7 @@ reads for a copy of known size), read from profiles/block_gemm_prefill_traffic.j
 it is reported as null when the GEMM source has changed since those counters
 were taken.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-configs] [--no-cpu]
        python bench.py --profile-workload NAME [--iters N]   (one kernel, for rocprofv3)
        python bench.py --calibrate-copy                      (copy of known size, for rocprofv3)
 """
@@ -43,12 +51,31 @@ import os
 import sys
 import time
 
+
+def host_threads() -> int:
+    """Host threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set (the machine's share of its cores)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+if __name__ == "__main__":
+    # before numpy (and its OpenBLAS) is first imported
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", str(host_threads()))
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 M, N, K = 8192, 18432, 7168
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+ROTATE_BYTES = 1 << 30       # bandwidth workloads cycle through at least this much
 
 # algorithmic bytes per launch (what the method must move)
 ACT_QUANT_BYTES = M * K * 2 + M * K + M * (K // 128) * 4                 # 177,995,776
@@ -56,23 +83,46 @@ DEQUANT_BYTES = N * K + (N // 128) * (K // 128) * 4 + N * K * 2          # 396,3
 GEMM_FLOP = 2 * M * N * K                                                # 2,164,663,517,184
 
 
-def parse():
+def act_quant_bytes(rows, k):
+    return rows * k * 2 + rows * k + rows * (k // 128) * 4
+
+
+def dequant_bytes(n, k, out_bytes=2):
+    return n * k + (-(-n // 128)) * (-(-k // 128)) * 4 + n * k * out_bytes
+
+
+def weight_quant_bytes(n, k):
+    return n * k * 2 + n * k + (-(-n // 128)) * (-(-k // 128)) * 4
+
+
+def decode_bytes(m, n, k):
+    """Weight stream plus activation codes, scales and output of one decode GEMM."""
+    return m * k + m * (k // 128) * 4 + n * k + (-(-n // 128)) * (k // 128) * 4 + m * n * 2
+
+
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--cpu-rows", type=int, default=6144,
-                   help="activation rows in the CPU oracle sample (0 skips it)")
-    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+                   help="activation rows in the CPU oracle sample of the step (0 skips it)")
+    p.add_argument("--no-cpu", action="store_true", help="skip every CPU oracle timing")
+    p.add_argument("--no-configs", action="store_true", help="time the step only")
+    p.add_argument("--config-reps", type=int, default=30,
+                   help="timed launches per bandwidth-bound workload")
+    p.add_argument("--prefill-rows", type=int, default=128,
+                   help="activation rows in the CPU oracle sample of each prefill GEMM")
     p.add_argument("--profile-workload", default=None,
                    choices=["act_quant", "act_quant_ue8m0", "dequant", "dequant_ragged", "weight_quant",
                             "weight_quant_ue8m0", "decode1", "decode8", "decode32", "decode64",
-                            "act_quant_gemm1", "act_quant_gemm2", "prefill1", "prefill2"],
-                   help="run only this workload's kernel --iters times (for rocprofv3)")
+                            "act_quant_gemm1", "act_quant_gemm2", "act_quant_gemm8", "act_quant_gemm32",
+                            "act_quant_gemm64", "prefill1", "prefill2", "step"],
+                   help="run only this workload's kernels --iters times (for rocprofv3)")
     p.add_argument("--iters", type=int, default=20)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="copy 1 GiB once with torch (counter calibration under rocprofv3)")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
 GEMM_SOURCE = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc", "block_gemm.hip")
@@ -97,49 +147,75 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
+def copies(t, nbytes_each, total=ROTATE_BYTES):
+    """t and enough clones of it that all of them together span `total` bytes."""
+    n = max(1, -(-total // max(1, nbytes_each)))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+class Rotation:
+    """Cycles through a list of argument sets, one per call."""
+
+    def __init__(self, items):
+        self.items = items
+        self.i = 0
+
+    def next(self):
+        self.i += 1
+        return self.items[self.i % len(self.items)]
+
+
 def profile_workload(name, iters):
-    """Run one workload's kernel `iters` times (inputs resident in HBM)."""
+    """Run one workload's kernels `iters` times, inputs resident in HBM; the
+    bandwidth-bound ones cycle through >= 1 GB of buffer copies so that no
+    launch is served from the Infinity Cache."""
     import torch
 
     import fp8_block_scaled_quant_amd as fb
     from inputs import gen
 
     dev = torch.device("cuda:0")
-    # the decode workloads cycle through eight copies of the 132 MB weight so
-    # that every read comes from HBM, not the 256 MB Infinity Cache
-    step = [0]
-
-    def rotating(ws_list):
-        step[0] += 1
-        return ws_list[step[0] % len(ws_list)]
-
     if name.startswith("act_quant_gemm"):
         d = gen.decode_gemm(int(name[len("act_quant_gemm"):]))
         x = d["x"].to(dev)
         w0 = torch.from_numpy(d["w"]).to(dev)
-        wl = [w0] + [w0.clone() for _ in range(7)]
+        rot = Rotation(copies(w0, w0.numel()))
         ws = torch.from_numpy(d["w_s"]).to(dev)
-        run = lambda: fb.act_quant_gemm(x, rotating(wl), ws)
+        run = lambda: fb.act_quant_gemm(x, rot.next(), ws)
     elif name.startswith("act_quant"):
-        x = gen.act_quant_workload()["x"].to(dev)
+        x0 = gen.act_quant_workload()["x"].to(dev)
+        rot = Rotation(copies(x0, act_quant_bytes(M, K)))
         fmt = "ue8m0" if name.endswith("ue8m0") else None
-        run = lambda: fb.act_quant(x, 128, fmt)
+        run = lambda: fb.act_quant(rot.next(), 128, fmt)
     elif name.startswith("dequant"):
-        d = gen.dequant_workload(n=18440 if name.endswith("ragged") else 18432)
-        w = torch.from_numpy(d["w"]).to(dev)
+        n = 18440 if name.endswith("ragged") else 18432
+        d = gen.dequant_workload(n=n)
+        w0 = torch.from_numpy(d["w"]).to(dev)
         ws = torch.from_numpy(d["w_s"]).to(dev)
-        run = lambda: fb.weight_dequant(w, ws, 128, torch.bfloat16)
+        rot = Rotation(copies(w0, dequant_bytes(n, K)))
+        run = lambda: fb.weight_dequant(rot.next(), ws, 128, torch.bfloat16)
     elif name.startswith("weight_quant"):
-        w = gen.weight_quant_workload()["w"].to(dev)
+        w0 = gen.weight_quant_workload()["w"].to(dev)
+        rot = Rotation(copies(w0, weight_quant_bytes(N, K)))
         fmt = "ue8m0" if name.endswith("ue8m0") else None
-        run = lambda: fb.weight_quant(w, 128, fmt)
+        run = lambda: fb.weight_quant(rot.next(), 128, fmt)
     elif name.startswith("decode"):
         d = gen.decode_gemm(int(name[len("decode"):]))
         y, s = fb.act_quant(d["x"].to(dev))
         w0 = torch.from_numpy(d["w"]).to(dev)
-        wl = [w0] + [w0.clone() for _ in range(7)]
+        rot = Rotation(copies(w0, w0.numel()))
         ws = torch.from_numpy(d["w_s"]).to(dev)
-        run = lambda: fb.fp8_gemm(y, s, rotating(wl), ws, torch.bfloat16)
+        run = lambda: fb.fp8_gemm(y, s, rot.next(), ws, torch.bfloat16)
+    elif name == "step":
+        d = gen.prefill_gemm(1)
+        x = d["x"].to(dev)
+        w = torch.from_numpy(d["w"]).to(dev)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+
+        def run():
+            y, s = fb.act_quant(x, 128, "ue8m0")
+            fb.weight_dequant(w, ws, 128, torch.bfloat16)
+            fb.fp8_gemm(y, s, w, ws, torch.bfloat16, "ue8m0")
     else:
         d = gen.prefill_gemm(int(name[-1]))
         y, s = fb.act_quant(d["x"].to(dev), 128, "ue8m0")
@@ -204,15 +280,218 @@ class TimingEvents:
         self.events = []
 
 
+def time_launches(calls, reps, warmup, stream):
+    """Mean and median microseconds of each call in `calls` (callables run in
+    order, once per repetition), from events recorded between them on `stream`."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    nc = len(calls)
+    ev = TimingEvents((nc + 1) * reps)
+    for r in range(reps):
+        base = (nc + 1) * r
+        ev.record(base, stream)
+        for i, c in enumerate(calls):
+            c()
+            ev.record(base + i + 1, stream)
+    torch.cuda.synchronize()
+    out = []
+    for i in range(nc):
+        t = np.array([ev.elapsed_ms((nc + 1) * r + i, (nc + 1) * r + i + 1) for r in range(reps)]) * 1e3
+        out.append((float(t.mean()), float(np.median(t))))
+    whole = np.array([ev.elapsed_ms((nc + 1) * r, (nc + 1) * r + nc) for r in range(reps)]) * 1e3
+    ev.close()
+    return out, (float(whole.mean()), float(np.median(whole)))
+
+
+def timed_cpu(fn):
+    t0 = time.perf_counter()
+    out = fn()
+    return out, time.perf_counter() - t0
+
+
+def blas_info():
+    """numpy and OpenBLAS versions and the BLAS thread count in this process."""
+    import numpy as np
+    info = {"numpy": np.__version__, "blas": None, "blas_version": None, "blas_threads": None,
+            "OPENBLAS_NUM_THREADS": os.environ.get("OPENBLAS_NUM_THREADS")}
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                info.update(blas=i.get("internal_api"), blas_version=i.get("version"),
+                            blas_threads=i.get("num_threads"))
+                break
+    except Exception:
+        pass
+    return info
+
+
+def hbm_record(us, nbytes, extra=None):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    rec = {"us": us, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": nbytes}
+    rec.update(extra or {})
+    return rec
+
+
+def oracle_record(seconds, what, nbytes=None, flop=None):
+    rec = {"oracle_s": seconds, "oracle_sample": what}
+    if nbytes:
+        rec["oracle_GB/s"] = nbytes / seconds / 1e9
+    if flop:
+        rec["oracle_GFLOP/s"] = flop / seconds / 1e9
+    return rec
+
+
+def bench_configs(args, stream):
+    """Per-workload records: GPU time and rate, roofline fraction, oracle time."""
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_quant_amd as fb
+    import oracle
+    from inputs import gen
+
+    dev = torch.device("cuda:0")
+    reps, warm = args.config_reps, 5
+    cpu = not args.no_cpu
+    recs = {}
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # 1. tiny GEMM: fp32 activations [16, 512] -> act_quant (None) -> GEMM, fp32 out
+    d = gen.tiny_gemm()
+    x = d["x"].to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    ws = torch.from_numpy(d["w_s"]).to(dev)
+    y, s = fb.act_quant(x)
+    (aq, gm), _ = time_launches([lambda: fb.act_quant(x), lambda: fb.fp8_gemm(y, s, w, ws, torch.float32)],
+                                reps, warm, stream)
+    rec = {"workload": "tiny: act_quant fp32 [16,512] (scale_fmt None) + block GEMM 16x256x512, fp32 out",
+           "act_quant_us": aq[0], "gemm_us": gm[0], "gemm_flop": 2 * 16 * 256 * 512, "bound": "launch latency"}
+    if cpu:
+        xn = d["x"].numpy()
+        _, t = timed_cpu(lambda: oracle.fp8_gemm(*oracle.act_quant(xn), d["w"], d["w_s"]))
+        rec.update(oracle_record(t, "whole workload"))
+    recs["tiny"] = rec
+    log("tiny done")
+
+    # 2. act_quant [8192, 7168] bf16, both scale formats, rotating >= 1 GB
+    d = gen.act_quant_workload()
+    nbytes = act_quant_bytes(M, K)
+    xs = copies(d["x"].to(dev), nbytes)
+    xn = d["x"].float().numpy() if cpu else None
+    for fmt in (None, "ue8m0"):
+        rot = Rotation(xs)
+        (t,), _ = time_launches([lambda: fb.act_quant(rot.next(), 128, fmt)], reps, warm, stream)
+        rec = hbm_record(t[0], nbytes, {"median_us": t[1], "rotation": len(xs),
+                                        "workload": f"act_quant bf16 [8192,7168] scale_fmt={fmt}"})
+        if cpu:
+            _, tc = timed_cpu(lambda: oracle.act_quant(xn, 128, fmt))
+            rec.update(oracle_record(tc, "whole tensor", nbytes=nbytes))
+        recs[f"act_quant_{'ue8m0' if fmt else 'none'}"] = rec
+    del xs, xn
+    log("act_quant done")
+
+    # 3. weight_dequant [18432, 7168] and ragged [18440, 7168] -> bf16, rotating >= 1 GB
+    for n, key in ((18432, "dequant"), (18440, "dequant_ragged")):
+        d = gen.dequant_workload(n=n)
+        nbytes = dequant_bytes(n, K)
+        wl = copies(torch.from_numpy(d["w"]).to(dev), nbytes)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+        rot = Rotation(wl)
+        (t,), _ = time_launches([lambda: fb.weight_dequant(rot.next(), ws, 128, torch.bfloat16)], reps, warm,
+                                stream)
+        rec = hbm_record(t[0], nbytes, {"median_us": t[1], "rotation": len(wl),
+                                        "workload": f"weight_dequant E4M3 [{n},7168] -> bf16"})
+        if cpu:
+            _, tc = timed_cpu(lambda: oracle.weight_dequant(d["w"], d["w_s"], 128, "bf16"))
+            rec.update(oracle_record(tc, "whole tensor", nbytes=nbytes))
+        recs[key] = rec
+        del wl
+    log("dequant done")
+
+    # weight_quant (the GEMM's weight operand) bf16 [18432, 7168], rotating >= 1 GB
+    d = gen.weight_quant_workload()
+    nbytes = weight_quant_bytes(N, K)
+    wl = copies(d["w"].to(dev), nbytes)
+    for fmt in (None, "ue8m0"):
+        rot = Rotation(wl)
+        (t,), _ = time_launches([lambda: fb.weight_quant(rot.next(), 128, fmt)], reps, warm, stream)
+        recs[f"weight_quant_{'ue8m0' if fmt else 'none'}"] = hbm_record(
+            t[0], nbytes, {"median_us": t[1], "rotation": len(wl),
+                           "workload": f"weight_quant bf16 [18432,7168] scale_fmt={fmt}"})
+    del wl
+    log("weight_quant done")
+
+    # 4. decode GEMMs: weights cycle through >= 1 GB of copies
+    for m in (1, 8, 32, 64):
+        d = gen.decode_gemm(m)
+        x = d["x"].to(dev)
+        wl = copies(torch.from_numpy(d["w"]).to(dev), N * K)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+        y, s = fb.act_quant(x)
+        rot = Rotation(wl)
+        (gm,), _ = time_launches([lambda: fb.fp8_gemm(y, s, rot.next(), ws, torch.bfloat16)], reps, warm, stream)
+        rot = Rotation(wl)
+        (aq, gm2), pair = time_launches([lambda: fb.act_quant(x),
+                                         lambda: fb.fp8_gemm(y, s, rot.next(), ws, torch.bfloat16)],
+                                        reps, warm, stream)
+        rot = Rotation(wl)
+        (fu,), _ = time_launches([lambda: fb.act_quant_gemm(x, rot.next(), ws)], reps, warm, stream)
+        nbytes = decode_bytes(m, N, K)
+        flop = 2 * m * N * K
+        rec = hbm_record(gm[0], nbytes, {
+            "workload": f"decode GEMM M={m} N=18432 K=7168, bf16 out (activations quantized by act_quant, None)",
+            "median_us": gm[1], "TFLOP/s": flop / (gm[0] * 1e-6) / 1e12, "rotation": len(wl),
+            "act_quant_us": aq[0], "act_quant_then_gemm_us": pair[0],
+            "act_quant_gemm_call_us": fu[0]})
+        if cpu:
+            xn = d["x"].float().numpy()
+            _, tc = timed_cpu(lambda: oracle.fp8_gemm(*oracle.act_quant(xn), d["w"], d["w_s"]))
+            rec.update(oracle_record(tc, "whole workload (act_quant + GEMM)", flop=flop))
+        recs[f"decode_m{m}"] = rec
+        del wl
+    log("decode done")
+
+    # 5. prefill GEMMs, ue8m0 activation scales, bf16 out (shape 2 may split its last round over K)
+    for shape in (1, 2):
+        d = gen.prefill_gemm(shape)
+        n, k = d["w"].shape
+        x = d["x"].to(dev)
+        w = torch.from_numpy(d["w"]).to(dev)
+        ws = torch.from_numpy(d["w_s"]).to(dev)
+        y, s = fb.act_quant(x, 128, "ue8m0")
+        # enough warm-up launches (~20 ms) for the clock to settle after the idle host-side work
+        (aq, gm), _ = time_launches([lambda: fb.act_quant(x, 128, "ue8m0"),
+                                     lambda: fb.fp8_gemm(y, s, w, ws, torch.bfloat16, "ue8m0")],
+                                    max(5, reps // 2), 20, stream)
+        flop = 2 * M * n * k
+        tf = flop / (gm[0] * 1e-6) / 1e12
+        rec = {"workload": f"prefill GEMM {M}x{n}x{k}, ue8m0 activation scales, bf16 out",
+               "us": gm[0], "median_us": gm[1], "TFLOP/s": tf, "frac_mfma": tf / PEAK_FP8_TFLOPS, "flop": flop,
+               "act_quant_us": aq[0], "act_quant_bytes": act_quant_bytes(M, k)}
+        if cpu and args.prefill_rows > 0:
+            rows = args.prefill_rows
+            xn = d["x"][:rows].float().numpy()
+            _, tc = timed_cpu(lambda: oracle.fp8_gemm(*oracle.act_quant(xn, 128, "ue8m0"), d["w"], d["w_s"]))
+            rec.update(oracle_record(tc, f"first {rows} of {M} rows (act_quant + GEMM, all {n} columns)",
+                                     flop=2 * rows * n * k))
+        recs[f"prefill_shape{shape}"] = rec
+        del x, w, y
+    log("prefill done")
+    return recs
+
+
 def cpu_baseline(x_bf16, w, ws, rows):
     """Time the oracle on the first `rows` rows (and rows/M of the weight)."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = None
+    info = blas_info()
     x = x_bf16[:rows].float().numpy()
     wrows = max(128, (N * rows // M) // 128 * 128)
     t0 = time.perf_counter()
@@ -221,21 +500,23 @@ def cpu_baseline(x_bf16, w, ws, rows):
     oracle.fp8_gemm(a, a_s, w, ws)
     dt = time.perf_counter() - t0
     flop = 2.0 * rows * N * K
-    cores = len(os.sched_getaffinity(0))
+    cores = info["blas_threads"] or host_threads()
     return {
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": blas_threads if blas_threads else cores,
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"first {rows} of {M} activation rows through act_quant(ue8m0) + fp8_gemm "
                    f"(all {N} columns) and {wrows} of {N} weight rows through weight_dequant; "
-                   f"{dt:.2f} s; value = 2*{rows}*N*K / time; host has {cores} usable cores"),
+                   f"{dt:.2f} s; value = 2*{rows}*N*K / time; {cores} BLAS threads "
+                   f"(elementwise steps single-threaded numpy)"),
         "seconds": dt,
+        "host": info,
     }
 
 
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     if args.profile_workload:
         profile_workload(args.profile_workload, args.iters)
         return
@@ -314,8 +595,9 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {
-            "workload": ("prefill linear layer: act_quant ue8m0 of bf16 [8192,7168] + weight_dequant "
-                         "[18432,7168]->bf16 + block-scaled FP8 GEMM 8192x18432x7168, bf16 out"),
+            "workload": ("one pass of the hot path, three kernels: act_quant (ue8m0) of bf16 [8192,7168]; "
+                         "weight_dequant of E4M3 [18432,7168] with [144,56] scales -> bf16 (not read by the "
+                         "GEMM); block-scaled FP8 GEMM 8192x18432x7168 (fp8_block_gemm_ue8m0), bf16 out"),
             "m": M, "n": N, "k": K, "scale_fmt": "ue8m0", "out": "bf16",
         },
         "roofline": {
@@ -336,6 +618,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    del x, w
+    if not args.no_configs:
+        result["configs"] = bench_configs(args, stream)
     if not args.no_cpu and args.cpu_rows > 0:
         result["cpu_baseline"] = cpu_baseline(x_cpu, w_np, ws_np, args.cpu_rows)
     print(json.dumps(result), flush=True)

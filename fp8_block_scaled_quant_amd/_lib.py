@@ -16,8 +16,9 @@ SCALE_NONE, SCALE_UE8M0 = 0, 1
 
 # every symbol include/fp8bsq.h declares
 EXPORTS = ("fp8_act_quant", "fp8_weight_dequant", "fp8_weight_quant", "fp8_block_gemm",
-           "fp8_block_gemm_ue8m0", "fp8_block_gemm_split", "fp8_block_gemm_split_workspace",
-           "fp8_act_quant_gemm", "fp8bsq_strerror", "fp8bsq_version")
+           "fp8_block_gemm_ue8m0", "fp8_block_gemm_reference", "fp8_block_gemm_split",
+           "fp8_block_gemm_split_workspace", "fp8_act_quant_gemm", "fp8bsq_strerror",
+           "fp8bsq_version")
 
 _LIB = None
 
@@ -53,6 +54,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.fp8_block_gemm.restype = i32
     lib.fp8_block_gemm_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     lib.fp8_block_gemm_ue8m0.restype = i32
+    lib.fp8_block_gemm_reference.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    lib.fp8_block_gemm_reference.restype = i32
     lib.fp8_block_gemm_split.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp,
                                          ctypes.c_size_t, vp]
     lib.fp8_block_gemm_split.restype = i32

@@ -65,9 +65,11 @@ int fp8_weight_quant(const void *x, int x_dtype, int64_t m, int64_t n, int block
 
 namespace {
 
+enum class GemmKernel { kDispatch, kDispatchPow2, kReference };
+
 int block_gemm_checked(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
                        void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream,
-                       bool a_s_pow2) {
+                       GemmKernel kernel) {
   if (!a || !a_s || !b || !b_s || !c) return FP8BSQ_EINVAL;
   if (m <= 0 || n <= 0 || k <= 0) return FP8BSQ_EINVAL;
   if (c_dtype != FP8BSQ_F32 && c_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
@@ -76,20 +78,30 @@ int block_gemm_checked(const uint8_t *a, const float *a_s, const uint8_t *b, con
       !aligned(c, 4))
     return FP8BSQ_EALIGN;
   if (m > kMaxGemmRows || n >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
-  return launch_status(fp8bsq::launch_block_gemm(a, a_s, b, b_s, c, c_dtype == FP8BSQ_BF16, m, n,
-                                                 k, (hipStream_t)hip_stream, nullptr, a_s_pow2));
+  const bool bf16 = c_dtype == FP8BSQ_BF16;
+  const hipStream_t st = (hipStream_t)hip_stream;
+  if (kernel == GemmKernel::kReference)
+    return launch_status(fp8bsq::launch_block_gemm_reference(a, a_s, b, b_s, c, bf16, m, n, k, st));
+  return launch_status(fp8bsq::launch_block_gemm(a, a_s, b, b_s, c, bf16, m, n, k, st, nullptr,
+                                                 kernel == GemmKernel::kDispatchPow2));
 }
 
 }  // namespace
 
 int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
                    void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
-  return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream, false);
+  return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream, GemmKernel::kDispatch);
 }
 
 int fp8_block_gemm_ue8m0(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
                          void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
-  return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream, true);
+  return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream,
+                            GemmKernel::kDispatchPow2);
+}
+
+int fp8_block_gemm_reference(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
+                             void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream) {
+  return block_gemm_checked(a, a_s, b, b_s, c, c_dtype, m, n, k, hip_stream, GemmKernel::kReference);
 }
 
 size_t fp8_block_gemm_split_workspace(int64_t m, int64_t n, int64_t k) {

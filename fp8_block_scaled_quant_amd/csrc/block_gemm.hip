@@ -16,6 +16,8 @@
 // same lane/byte -> k assignment, so the product is the block's full dot
 // product whatever order the hardware pairs the bytes in.  The 16x16 FP32
 // result sits in lane l as column (l % 16), rows 4 * (l / 16) + 0..3.
+#include <atomic>
+
 #include "launch.h"
 #include "quant_common.h"
 
@@ -915,17 +917,34 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
 
 }  // namespace
 
-// Diagnostic: FP8BSQ_GEMM_REFERENCE=1 in the environment sends every GEMM to
-// the reference-structure kernel (read on each call).
-static bool reference_kernel_forced() {
-  const char *v = getenv("FP8BSQ_GEMM_REFERENCE");
-  return v && v[0] == '1';
+// Compute units of the current device, asked of the runtime once per device;
+// 0 if the runtime cannot say.
+static int current_device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];   // 0: not asked yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 // the tiled kernel serves m > 64 while A, B and a_s fit its 32-bit per-lane offsets
 static bool tiled_path(int64_t m, int64_t n, int64_t k) {
-  return !reference_kernel_forced() && m > 64 && m * k < ((int64_t)1 << 32) &&
-         n * k < ((int64_t)1 << 32);
+  return m > 64 && m * k < ((int64_t)1 << 32) && n * k < ((int64_t)1 << 32);
+}
+
+// The tiled kernel applies power-of-two activation scales inside the
+// MX-scaled MFMA when they come from the scale table (K / 128 a multiple of 4,
+// a_s 16-byte aligned); otherwise it applies a_s in the FP32 rescale.
+static bool mx_kernel_used(int64_t k, const float *a_s, bool a_s_pow2) {
+  return a_s_pow2 && (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
 }
 
 // Tiled kernel: unsplit, tiles [0, grid) by min(grid, CUs) persistent
@@ -938,10 +957,8 @@ static hipError_t launch_tiles(const uint8_t *a, const float *a_s, const uint8_t
                                uint32_t *counters, int zero_n = 0) {
   const int tiles_m = (int)((m + kTileM - 1) / kTileM), tiles_n = (int)((n + kTileN - 1) / kTileN);
   const dim3 block(kThreads);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  int cus = current_device_cus();
+  if (cus <= 0) cus = 256;
   const unsigned pgrid = grid < (unsigned)cus ? grid : (unsigned)cus;
 #define FP8BSQ_TILE(BF16, MX, TAB)                                                                      \
   do {                                                                                                   \
@@ -956,12 +973,13 @@ static hipError_t launch_tiles(const uint8_t *a, const float *a_s, const uint8_t
   // the scale table loads each row's scales in 16-byte pieces; the MX-scaled
   // kernel reads its exponents from it
   const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
+  const bool mx = mx_kernel_used(k, a_s, a_s_pow2);
   if (c_bf16) {
-    if (tab && a_s_pow2) FP8BSQ_TILE(true, true, true);
+    if (mx) FP8BSQ_TILE(true, true, true);
     else if (tab) FP8BSQ_TILE(true, false, true);
     else FP8BSQ_TILE(true, false, false);
   } else {
-    if (tab && a_s_pow2) FP8BSQ_TILE(false, true, true);
+    if (mx) FP8BSQ_TILE(false, true, true);
     else if (tab) FP8BSQ_TILE(false, false, true);
     else FP8BSQ_TILE(false, false, false);
   }
@@ -971,6 +989,60 @@ static hipError_t launch_tiles(const uint8_t *a, const float *a_s, const uint8_t
 
 __global__ void zero_u32_kernel(uint32_t *p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// Guard of the MX-scaled kernel, which applies each activation scale as the
+// E8M0 exponent field of its fp32 bits: a row of a_s [m, nkb] holding any
+// value that is not a positive normal power of two (bits other than e << 23,
+// 1 <= e <= 254) gets NaN in every column of its C row.  Runs after the GEMM
+// on the same stream.  64 rows per workgroup, four lanes per row.
+constexpr int kGuardRows = 64;
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void ue8m0_guard_kernel(const float *__restrict__ a_s, int64_t m,
+                                                          int nkb, void *__restrict__ c, int64_t n) {
+  __shared__ uint32_t bad[kGuardRows];
+  __shared__ int any_bad;
+  const int t = threadIdx.x;
+  if (t < kGuardRows) bad[t] = 0u;
+  if (t == 0) any_bad = 0;
+  __syncthreads();
+  const int64_t row = (int64_t)blockIdx.x * kGuardRows + t / 4;
+  if (row < m) {
+    const uint32_t *r = (const uint32_t *)a_s + row * nkb;
+    uint32_t stray = 0u, low = 0xFFFFFFFFu;
+    for (int j = t % 4; j < nkb; j += 4) {
+      const uint32_t v = r[j];
+      stray |= v & 0x807FFFFFu;   // sign or mantissa bits
+      low = v < low ? v : low;    // zero or subnormal exponent
+    }
+    if (stray != 0u || low < 0x00800000u) {
+      bad[t / 4] = 1u;
+      any_bad = 1;
+    }
+  }
+  __syncthreads();
+  if (!any_bad) return;
+  for (int i = 0; i < kGuardRows; ++i) {
+    const int64_t rr = (int64_t)blockIdx.x * kGuardRows + i;
+    if (rr >= m || !bad[i]) continue;
+    for (int64_t j = t; j < n; j += 256) {
+      if (kBf16Out)
+        ((uint16_t *)c)[rr * n + j] = 0x7FC0u;
+      else
+        ((uint32_t *)c)[rr * n + j] = 0x7FC00000u;
+    }
+  }
+}
+
+static hipError_t launch_ue8m0_guard(const float *a_s, int64_t m, int64_t k, void *c, bool c_bf16,
+                                     int64_t n, hipStream_t stream) {
+  const dim3 grid((unsigned)((m + kGuardRows - 1) / kGuardRows)), block(256);
+  const int nkb = (int)(k / kBlock);
+  if (c_bf16)
+    hipLaunchKernelGGL(ue8m0_guard_kernel<true>, grid, block, 0, stream, a_s, m, nkb, c, n);
+  else
+    hipLaunchKernelGGL(ue8m0_guard_kernel<false>, grid, block, 0, stream, a_s, m, nkb, c, n);
+  return hipGetLastError();
 }
 
 // Split-K plan: when the tiles leave a last round that fills at most half the
@@ -985,10 +1057,8 @@ struct SplitPlan {
 static SplitPlan split_plan(int64_t m, int64_t n, int64_t k) {
   SplitPlan p;
   if (!tiled_path(m, n, k)) return p;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return p;
+  const int cus = current_device_cus();
+  if (cus <= 0) return p;
   const int64_t tiles = ((m + kTileM - 1) / kTileM) * ((n + kTileN - 1) / kTileN);
   const int full = (int)(tiles / cus * cus), tail = (int)(tiles - full);
   const int nkb = (int)(k / kBlock), nch = (nkb + kTabKb - 1) / kTabKb;
@@ -1028,22 +1098,26 @@ hipError_t launch_block_gemm_split(const uint8_t *a, const float *a_s, const uin
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_tiles(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, nullptr, a_s_pow2,
-                      (unsigned)(p.tail * p.parts), true, p.full, p.parts, partials, counters);
+  const hipError_t e = launch_tiles(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, nullptr, a_s_pow2,
+                                    (unsigned)(p.tail * p.parts), true, p.full, p.parts, partials,
+                                    counters);
+  if (e != hipSuccess || !mx_kernel_used(k, a_s, a_s_pow2)) return e;
+  return launch_ue8m0_guard(a_s, m, k, c, c_bf16, n, stream);
 }
 
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream, const void *bias, bool a_s_pow2) {
-  const bool reference = reference_kernel_forced();
   if (tiled_path(m, n, k)) {
     const int64_t tiles = ((m + kTileM - 1) / kTileM) * ((n + kTileN - 1) / kTileN);
-    return launch_tiles(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, bias, a_s_pow2, (unsigned)tiles,
-                        false, 0, 1, nullptr, nullptr);
+    const hipError_t e = launch_tiles(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, bias, a_s_pow2,
+                                      (unsigned)tiles, false, 0, 1, nullptr, nullptr);
+    if (e != hipSuccess || !mx_kernel_used(k, a_s, a_s_pow2)) return e;
+    return launch_ue8m0_guard(a_s, m, k, c, c_bf16, n, stream);
   }
   // the decode kernel's A and weight transfers use 32-bit lane offsets (from A's
   // base, and from each wave's first weight row)
-  if (!reference && m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && 16 * k < ((int64_t)1 << 32)) {
+  if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && 16 * k < ((int64_t)1 << 32)) {
     const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * (kDecodeCompute + 1));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
 #define FP8BSQ_DECODE_T(MT, TAB)                                                                          \
@@ -1069,6 +1143,12 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
 #undef FP8BSQ_DECODE_T
     return hipGetLastError();
   }
+  return launch_block_gemm_reference(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, bias);
+}
+
+hipError_t launch_block_gemm_reference(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                       const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                                       int64_t k, hipStream_t stream, const void *bias) {
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), block(256);
   if (c_bf16)
     hipLaunchKernelGGL(block_gemm_simple_kernel<true>, grid, block, 0, stream, a, a_s, b, b_s, c,

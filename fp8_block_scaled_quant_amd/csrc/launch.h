@@ -23,15 +23,24 @@ hipError_t launch_weight_quant(const void *x, bool x_bf16, int64_t m, int64_t n,
 
 // C[m, n] = block-scaled A[m, k] . B[n, k]^T (+ bias[n] of C's dtype, if not null).
 // a_s_pow2: every a_s is a power of two (act_quant ue8m0), so the tiled kernel
-// may apply it inside the MX-scaled MFMA.
+// may apply it inside the MX-scaled MFMA; when it does, a guard kernel queued
+// after it sets to NaN every C row whose a_s row breaks that precondition.
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,
                              const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
                              int64_t k, hipStream_t stream, const void *bias = nullptr,
                              bool a_s_pow2 = false);
 
+// The same product by the reference-structure kernel (fragments straight from
+// global memory), for any shape: what shapes beyond the fast kernels' 32-bit
+// offsets take.
+hipError_t launch_block_gemm_reference(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                       const float *b_s, void *c, bool c_bf16, int64_t m, int64_t n,
+                                       int64_t k, hipStream_t stream, const void *bias = nullptr);
+
 // launch_block_gemm with split-K for a last round of tiles that would leave
 // CUs idle.  workspace: block_gemm_split_bytes(m, n, k) bytes, 256-byte
-// aligned, whose leading counters are zero on entry and again on completion.
+// aligned, with no initial contents required: the call clears the tail's
+// counters itself (in its first launch) and leaves them at the part count.
 // With a smaller workspace (or when no split pays), the same launch as
 // launch_block_gemm.
 size_t block_gemm_split_bytes(int64_t m, int64_t n, int64_t k);

@@ -155,9 +155,6 @@ FP8BSQ_API int fp8_weight_quant(const void *x, int x_dtype, int64_t m, int64_t n
  *
  * Accumulation order is not specified; every element is within
  * 1e-3 * sum_k |a_k * b_k| of the exact result (plus one bf16 ulp for BF16).
- * Diagnostic: with FP8BSQ_GEMM_REFERENCE=1 in the environment (read on each
- * call) every GEMM entry point uses the slow reference-structure kernel that
- * otherwise serves only shapes beyond the fast kernels' 32-bit offsets.
  */
 FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b, const float *b_s,
                    void *c, int c_dtype, int64_t m, int64_t n, int64_t k, void *hip_stream);
@@ -176,12 +173,31 @@ FP8BSQ_API int fp8_block_gemm(const uint8_t *a, const float *a_s, const uint8_t 
  * the same inputs.
  *
  * Arguments, layouts and errors as for fp8_block_gemm.  Precondition: every
- * a_s value is a positive normal power of two; other values give unspecified
- * (memory-safe) results.
+ * a_s value is a positive normal power of two.  Where the MX-scaled kernel
+ * runs (m > 64, k / 128 a multiple of 4, a_s 16-byte aligned) the call checks
+ * it with a second kernel queued after the product: every C row whose a_s row
+ * holds any other value is set to NaN in all n columns.  Other shapes run
+ * fp8_block_gemm's kernels, which apply any a_s exactly.
  */
 FP8BSQ_API int fp8_block_gemm_ue8m0(const uint8_t *a, const float *a_s, const uint8_t *b,
                          const float *b_s, void *c, int c_dtype, int64_t m, int64_t n, int64_t k,
                          void *hip_stream);
+
+/*
+ * fp8_block_gemm_reference -- fp8_block_gemm by its reference-structure
+ * kernel, for testing: each wave reads its MFMA fragments straight from
+ * global memory (no LDS staging, no persistent tiles).  This kernel is also
+ * what fp8_block_gemm runs for shapes beyond its fast kernels' 32-bit lane
+ * offsets (A or B of 4 GiB or more); this entry point runs it for any shape,
+ * so that path can be checked on small problems.
+ *
+ * Same product, arguments, layouts, bound and errors as fp8_block_gemm (page
+ * "How weight_dequant Handles Per-Block Scaling in DeepSeek-V3 FP8 GEMM",
+ * section "Relationship to FP8 GEMM Operations").  Slow: not for production.
+ */
+FP8BSQ_API int fp8_block_gemm_reference(const uint8_t *a, const float *a_s, const uint8_t *b,
+                             const float *b_s, void *c, int c_dtype, int64_t m, int64_t n,
+                             int64_t k, void *hip_stream);
 
 /*
  * fp8_block_gemm_split -- fp8_block_gemm / fp8_block_gemm_ue8m0 (scale_fmt

@@ -108,8 +108,12 @@ def weight_dequant(w: np.ndarray, s: np.ndarray, out: str = "bf16", offset: int 
 
 
 def block_gemm(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray, out: str = "bf16",
-               a_dev: torch.Tensor = None, a_s_dev: torch.Tensor = None, ue8m0: bool = False):
-    """Returns C as float64 numpy (bf16 widened exactly)."""
+               a_dev: torch.Tensor = None, a_s_dev: torch.Tensor = None, ue8m0: bool = False,
+               entry: str = None):
+    """Returns C as float64 numpy (bf16 widened exactly).
+
+    ``entry`` names the C entry point (default fp8_block_gemm, or
+    fp8_block_gemm_ue8m0 when ``ue8m0``)."""
     dev = device()
     m, k = a.shape if a is not None else a_dev.shape
     n = b.shape[0]
@@ -119,7 +123,9 @@ def block_gemm(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray, o
     bsd = torch.from_numpy(b_s).to(dev)
     esz = 2 if out == "bf16" else 4
     c = Guarded(m * n * esz)
-    fn = _lib.lib().fp8_block_gemm_ue8m0 if ue8m0 else _lib.lib().fp8_block_gemm
+    if entry is None:
+        entry = "fp8_block_gemm_ue8m0" if ue8m0 else "fp8_block_gemm"
+    fn = getattr(_lib.lib(), entry)
     st = fn(ctypes.c_void_p(ad.data_ptr()), ctypes.c_void_p(asd.data_ptr()),
                                    ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(bsd.data_ptr()),
                                    ctypes.c_void_p(c.ptr), _lib.BF16 if out == "bf16" else _lib.F32,

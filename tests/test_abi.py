@@ -1,8 +1,15 @@
 """C-ABI checks that need no GPU: the library loads, exports exactly the
 symbols include/fp8bsq.h declares, and rejects bad arguments with the
 documented status codes before touching HIP (no kernel is launched here; the
-pointers passed are never dereferenced because validation fails first)."""
+pointers passed are never dereferenced because validation fails first).
 
+With FP8BSQ_TEST_LIB naming the host-stub build of the ABI layer (abi.cpp
+over tests/abi_host_stub.cpp, made by test_abi_sanitized.py under
+AddressSanitizer and UndefinedBehaviorSanitizer), the same checks run against
+it, and so do the dispatch checks at the end, which call every entry point with
+valid arguments and read back which launcher the stub saw, with what."""
+
+import ctypes
 import os
 import re
 import subprocess
@@ -13,6 +20,7 @@ from fp8_block_scaled_quant_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8bsq.h")
+LIB_PATH = os.environ.get("FP8BSQ_TEST_LIB") or _lib.LIB_PATH
 
 
 def declared_symbols():
@@ -22,7 +30,7 @@ def declared_symbols():
 
 @pytest.fixture(scope="module")
 def lib():
-    return _lib.load_library()
+    return _lib.load_library(None if LIB_PATH == _lib.LIB_PATH else LIB_PATH)
 
 
 def test_header_declares_entry_points():
@@ -30,7 +38,7 @@ def test_header_declares_entry_points():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True)
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
     public = {s for s in exported if not s.startswith("_")}
     assert public == declared_symbols()
@@ -84,7 +92,7 @@ def test_weight_dequant_validation(lib):
     assert f(P, P, 1 << 31, 8, 128, P, 1, None) == _lib.ERANGE
 
 
-@pytest.mark.parametrize("name", ["fp8_block_gemm", "fp8_block_gemm_ue8m0"])
+@pytest.mark.parametrize("name", ["fp8_block_gemm", "fp8_block_gemm_ue8m0", "fp8_block_gemm_reference"])
 def test_block_gemm_validation(lib, name):
     f = getattr(lib, name)
     assert f(None, P, P, P, P, 1, 16, 16, 128, None) == _lib.EINVAL
@@ -154,3 +162,84 @@ def test_act_quant_gemm_validation(lib):
     assert call(a12=P + 2) == _lib.EALIGN
     assert call(a5=P + 1) == _lib.EALIGN          # bf16 bias must be 2-byte aligned
     assert call(a8=1 << 40) == _lib.ERANGE
+
+
+# ------------------------------------------------ dispatch (host-stub build only)
+
+class Stub:
+    def __init__(self, lib):
+        if not hasattr(lib, "_fp8bsq_stub_last"):
+            pytest.skip("dispatch checks need the host-stub build (test_abi_sanitized.py)")
+        self.lib = lib
+        lib._fp8bsq_stub_last.restype = ctypes.c_int
+        lib._fp8bsq_stub_last.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_void_p)]
+
+    def last(self):
+        name = ctypes.create_string_buffer(64)
+        ints = (ctypes.c_int64 * 16)()
+        ptrs = (ctypes.c_void_p * 12)()
+        n = self.lib._fp8bsq_stub_last(name, 64, ints, ptrs)
+        return n, name.value.decode(), list(ints), [p or 0 for p in ptrs]
+
+
+def test_dispatch_quantizers(lib):
+    st = Stub(lib)
+    S = 0x7000
+    assert lib.fp8_act_quant(P, 1, 8, 256, 128, 1, P + 16, P + 32, S) == _lib.OK
+    _, name, ints, ptrs = st.last()
+    assert name == "act_quant" and ints[:3] == [1, 16, 1] and ptrs[:4] == [P, P + 16, P + 32, S]
+    assert lib.fp8_act_quant(P, 0, 3, 384, 128, 0, P, P, None) == _lib.OK
+    assert st.last()[2][:3] == [0, 9, 0]
+    assert lib.fp8_weight_dequant(P + 1, P, 300, 130, 128, P + 2, 1, S) == _lib.OK
+    _, name, ints, ptrs = st.last()
+    assert name == "weight_dequant" and ints[:3] == [300, 130, 1] and ptrs[:4] == [P + 1, P, P + 2, S]
+    assert lib.fp8_weight_quant(P, 1, 300, 130, 128, 1, P + 8, P + 4, S) == _lib.OK
+    _, name, ints, ptrs = st.last()
+    assert name == "weight_quant" and ints[:4] == [1, 300, 130, 1] and ptrs[:4] == [P, P + 8, P + 4, S]
+
+
+def test_dispatch_gemms(lib):
+    st = Stub(lib)
+    S = 0x7000
+    a, a_s, b, b_s, c = P, P + 0x100, P + 0x200, P + 0x300, P + 0x400
+    for fn, name, pow2 in [("fp8_block_gemm", "block_gemm", 0), ("fp8_block_gemm_ue8m0", "block_gemm", 1),
+                           ("fp8_block_gemm_reference", "block_gemm_reference", None)]:
+        assert getattr(lib, fn)(a, a_s, b, b_s, c, 1, 300, 700, 1024, S) == _lib.OK
+        _, got, ints, ptrs = st.last()
+        assert got == name and ints[:4] == [1, 300, 700, 1024], fn
+        assert ptrs[:7] == [a, a_s, b, b_s, c, S, 0], fn       # bias null
+        if pow2 is not None:
+            assert ints[4] == pow2, fn
+    assert lib.fp8_block_gemm_split_workspace(300, 700, 1024) == 300 * 1000000 + 700 * 1000 + 1024
+    assert lib.fp8_block_gemm_split(a, a_s, b, b_s, c, 0, 300, 700, 1024, 1, P + 0x1000, 5000, S) == _lib.OK
+    _, got, ints, ptrs = st.last()
+    assert got == "block_gemm_split" and ints[:6] == [0, 300, 700, 1024, 1, 5000]
+    assert ptrs[:7] == [a, a_s, b, b_s, c, S, P + 0x1000]
+    assert lib.fp8_block_gemm_split(a, a_s, b, b_s, c, 0, 300, 700, 1024, 0, None, 5000, S) == _lib.OK
+    assert st.last()[2][4:6] == [0, 0]                      # no workspace: zero bytes passed on
+
+
+def test_dispatch_act_quant_gemm(lib):
+    st = Stub(lib)
+    S = 0x7000
+    x, b, b_s, bias, c, a_q, a_s = P, P + 0x100, P + 0x200, P + 0x300, P + 0x400, P + 0x500, P + 0x600
+    n0 = st.last()[0]
+    assert lib.fp8_act_quant_gemm(x, 1, 1, b, b_s, bias, c, 1, 2, 256, 512, a_q, a_s, S) == _lib.OK
+    n1, name, ints, ptrs = st.last()
+    assert n1 == n0 + 1 and name == "act_quant_gemm_fused"
+    assert ints[:5] == [1, 1, 2, 256, 512] and ptrs[:8] == [x, b, b_s, bias, c, a_q, a_s, S]
+    assert lib.fp8_act_quant_gemm(x, 1, 0, b, b_s, None, c, 0, 40, 256, 512, a_q, a_s, S) == _lib.OK
+    n2, name, ints, ptrs = st.last()
+    assert n2 == n1 + 2 and name == "block_gemm"           # act_quant, then the GEMM
+    assert ints[:5] == [0, 40, 256, 512, 0] and ptrs[:7] == [a_q, a_s, b, b_s, c, S, 0]
+
+
+def test_launch_error_maps_to_elaunch(lib):
+    Stub(lib)
+    lib._fp8bsq_stub_fail_next.restype = None
+    lib._fp8bsq_stub_fail_next()
+    assert lib.fp8_act_quant(P, 1, 8, 256, 128, 0, P, P, None) == _lib.ELAUNCH
+    assert lib.fp8_act_quant(P, 1, 8, 256, 128, 0, P, P, None) == _lib.OK
+    lib._fp8bsq_stub_fail_next()
+    assert lib.fp8_act_quant_gemm(P, 1, 0, P, P, None, P, 1, 40, 256, 512, P, P, None) == _lib.ELAUNCH

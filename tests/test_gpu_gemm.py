@@ -6,7 +6,7 @@ plus one bf16 ulp of C for BF16 output; NaN/Inf always fail.
 Cases: the tiny workload (fp32 activations [16, 512] quantized by the GPU
 act_quant, weights [256, 512], fp32 out); the decode workloads (M = 1, 8, 32,
 64, N = 18432, K = 7168, bf16 out), checked on every element; both prefill
-shapes at full size (M = 8192) checked on sampled rows (first, last and 254
+shapes at full size (M = 8192) checked on sampled rows (first, last and 512
 random rows, every column); ragged shapes with partial tiles in M and N.
 """
 
@@ -66,7 +66,7 @@ def test_prefill_workloads_sampled_rows(shape):
     a, a_s = _quantized_activations(d["x"], "ue8m0")
     got = G.block_gemm(a, a_s, d["w"], d["w_s"], "bf16")
     rng = np.random.default_rng(100 + shape)
-    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 254, replace=False)]))
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 512, replace=False)]))
     _assert_close(got[rows], a, a_s, d["w"], d["w_s"], "bf16", rows=rows, label=f"prefill {shape}")
 
 
@@ -121,15 +121,14 @@ def test_scale_indexing_probe_tiled(m, aligned):
 
 
 @pytest.mark.parametrize("m,n,k", [(3, 200, 384), (100, 300, 1024), (257, 130, 640)])
-def test_reference_kernel(m, n, k, monkeypatch):
+def test_reference_kernel(m, n, k):
     """The reference-structure kernel (what shapes beyond the tiled and decode
-    kernels' 32-bit offsets take), forced by FP8BSQ_GEMM_REFERENCE=1."""
-    monkeypatch.setenv("FP8BSQ_GEMM_REFERENCE", "1")
+    kernels' 32-bit offsets take), through fp8_block_gemm_reference."""
     d = gen.custom_gemm(seed=5 * m + n, m=m, n=n, k=k, outliers=True)
     G.announce(f"gemm reference kernel m={m} n={n} k={k}")
     a, a_s = _quantized_activations(d["x"], None)
     for out in ("bf16", "f32"):
-        got = G.block_gemm(a, a_s, d["w"], d["w_s"], out)
+        got = G.block_gemm(a, a_s, d["w"], d["w_s"], out, entry="fp8_block_gemm_reference")
         _assert_close(got, a, a_s, d["w"], d["w_s"], out, label=f"reference {m}x{n}x{k}")
 
 

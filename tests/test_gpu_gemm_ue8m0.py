@@ -36,7 +36,8 @@ def test_prefill_workloads(shape):
     dev = G.device()
     a, a_s = fb.act_quant(d["x"].to(dev), 128, "ue8m0")
     got = _both(a.view(torch.uint8), a_s, d["w"], d["w_s"], "bf16")
-    rows = np.concatenate([[0, a.shape[0] - 1], np.random.default_rng(shape).choice(a.shape[0], 62, replace=False)])
+    rows = np.unique(np.concatenate([[0, a.shape[0] - 1],
+                                     np.random.default_rng(shape).choice(a.shape[0], 512, replace=False)]))
     an, asn = a.view(torch.uint8).cpu().numpy(), a_s.cpu().numpy()
     c = oracle.fp8_gemm(an, asn, d["w"], d["w_s"], rows=rows)
     tol = oracle.gemm_tolerance(an, asn, d["w"], d["w_s"], rows=rows)
@@ -87,3 +88,55 @@ def test_binding():
     a, a_s = fb.act_quant(d["x"].to(dev), 128, "ue8m0")
     w, ws = torch.from_numpy(d["w"]).to(dev), torch.from_numpy(d["w_s"]).to(dev)
     assert torch.equal(fb.fp8_gemm(a, a_s, w, ws, scale_fmt="ue8m0"), fb.fp8_gemm(a, a_s, w, ws))
+
+
+def _scales_with_strays(m, nkb, seed, stray_rows):
+    """Power-of-two scales, except one entry in each of `stray_rows`: a value
+    with mantissa bits, zero, a negative power of two, a subnormal."""
+    rng = np.random.default_rng(seed)
+    a_s = (2.0 ** rng.integers(-20, 0, (m, nkb))).astype(np.float32)
+    strays = [np.float32(0.3), np.float32(0.0), np.float32(-0.125), np.float32(2.0**-130)]
+    for i, r in enumerate(stray_rows):
+        a_s[r, rng.integers(nkb)] = strays[i % len(strays)]
+    return a_s
+
+
+def _check_guarded(got, want, stray_rows):
+    stray = np.zeros(got.shape[0], bool)
+    stray[list(stray_rows)] = True
+    assert np.isnan(got[stray]).all(), "rows with stray scales must be NaN"
+    assert np.array_equal(got[~stray].view(np.uint64), want[~stray].view(np.uint64))
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_guard_marks_rows_with_stray_scales(out):
+    """fp8_block_gemm_ue8m0 on the MX-scaled kernel checks its precondition:
+    rows whose scales are not all positive normal powers of two come back NaN,
+    the other rows bit-identical to fp8_block_gemm."""
+    m, n, k = 300, 256, 1024
+    rng = np.random.default_rng(61)
+    a = gen.weight_codes(rng, m, k)
+    b = gen.weight_codes(rng, n, k)
+    b_s = gen.log_uniform_scales(rng, gen.scale_grid(n, k), -14, -2)
+    stray_rows = [0, 5, 130, 255, 256, 299]
+    a_s = _scales_with_strays(m, k // 128, 62, stray_rows)
+    G.announce(f"gemm_ue8m0 guard m={m} n={n} k={k} {out}")
+    got = G.block_gemm(a, a_s, b, b_s, out, ue8m0=True)
+    want = G.block_gemm(a, a_s, b, b_s, out)
+    _check_guarded(got, want, stray_rows)
+
+
+def test_guard_on_split_path():
+    m, n, k = 512, 1024, 8192
+    rng = np.random.default_rng(63)
+    a = gen.weight_codes(rng, m, k)
+    b = gen.weight_codes(rng, n, k)
+    b_s = gen.log_uniform_scales(rng, gen.scale_grid(n, k), -14, -2)
+    stray_rows = [3, 511]
+    a_s = _scales_with_strays(m, k // 128, 64, stray_rows)
+    dev = G.device()
+    ad, asd = torch.from_numpy(a).to(dev), torch.from_numpy(a_s).to(dev)
+    G.announce(f"gemm_split ue8m0 guard m={m} n={n} k={k}")
+    got, _ = G.block_gemm_split(ad, asd, b, b_s, "bf16", ue8m0=True)
+    want, _ = G.block_gemm_split(ad, asd, b, b_s, "bf16", ue8m0=False)
+    _check_guarded(got, want, stray_rows)
