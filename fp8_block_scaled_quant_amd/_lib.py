@@ -10,15 +10,16 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bsq.so")
 
 # enums of include/fp8bsq.h
-OK, EINVAL, ESHAPE, EUNSUPPORTED, EALIGN, ELAUNCH, ERANGE = range(7)
+OK, EINVAL, ESHAPE, EUNSUPPORTED, EALIGN, ELAUNCH, ERANGE, ESCRATCH = range(8)
+SPLIT_SCRATCH_BYTES = 67109376   # FP8BSQ_SPLIT_SCRATCH_BYTES
 F32, BF16 = 0, 1
 SCALE_NONE, SCALE_UE8M0 = 0, 1
 
 # every symbol include/fp8bsq.h declares
 EXPORTS = ("fp8_act_quant", "fp8_weight_dequant", "fp8_weight_quant", "fp8_block_gemm",
            "fp8_block_gemm_ue8m0", "fp8_block_gemm_reference", "fp8_block_gemm_split",
-           "fp8_block_gemm_split_workspace", "fp8_act_quant_gemm", "fp8bsq_strerror",
-           "fp8bsq_version")
+           "fp8_block_gemm_split_workspace", "fp8_block_gemm_split_noalloc", "fp8_act_quant_gemm",
+           "fp8bsq_strerror", "fp8bsq_version")
 
 _LIB = None
 
@@ -59,6 +60,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.fp8_block_gemm_split.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp,
                                          ctypes.c_size_t, vp]
     lib.fp8_block_gemm_split.restype = i32
+    lib.fp8_block_gemm_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp]
+    lib.fp8_block_gemm_split_noalloc.restype = i32
     lib.fp8_block_gemm_split_workspace.argtypes = [i64, i64, i64]
     lib.fp8_block_gemm_split_workspace.restype = ctypes.c_size_t
     lib.fp8_act_quant_gemm.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, vp]

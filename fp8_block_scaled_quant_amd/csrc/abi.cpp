@@ -127,6 +127,24 @@ int fp8_block_gemm_split(const uint8_t *a, const float *a_s, const uint8_t *b, c
       scale_fmt == FP8BSQ_SCALE_UE8M0, workspace, workspace ? workspace_bytes : 0));
 }
 
+int fp8_block_gemm_split_noalloc(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                 const float *b_s, void *c, int c_dtype, int64_t m, int64_t n,
+                                 int64_t k, int scale_fmt, void *hip_stream) {
+  if (!a || !a_s || !b || !b_s || !c) return FP8BSQ_EINVAL;
+  if (m <= 0 || n <= 0 || k <= 0) return FP8BSQ_EINVAL;
+  if (c_dtype != FP8BSQ_F32 && c_dtype != FP8BSQ_BF16) return FP8BSQ_EINVAL;
+  if (scale_fmt != FP8BSQ_SCALE_NONE && scale_fmt != FP8BSQ_SCALE_UE8M0) return FP8BSQ_EINVAL;
+  if (k % 128 != 0) return FP8BSQ_ESHAPE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(c, 4))
+    return FP8BSQ_EALIGN;
+  if (m > kMaxGemmRows || n >= kMaxDim || k >= kMaxDim) return FP8BSQ_ERANGE;
+  bool too_big = false;
+  const int rc = launch_status(fp8bsq::launch_block_gemm_split_noalloc(
+      a, a_s, b, b_s, c, c_dtype == FP8BSQ_BF16, m, n, k, (hipStream_t)hip_stream,
+      scale_fmt == FP8BSQ_SCALE_UE8M0, &too_big));
+  return too_big ? FP8BSQ_ESCRATCH : rc;
+}
+
 int fp8_act_quant_gemm(const void *x, int x_dtype, int scale_fmt, const uint8_t *b,
                        const float *b_s, const void *bias, void *c, int c_dtype, int64_t m,
                        int64_t n, int64_t k, uint8_t *a_q, float *a_s, void *hip_stream) {
@@ -162,6 +180,7 @@ const char *fp8bsq_strerror(int status) {
     case FP8BSQ_EALIGN: return "pointer is not aligned as the entry point requires";
     case FP8BSQ_ELAUNCH: return "HIP runtime error at kernel launch";
     case FP8BSQ_ERANGE: return "size exceeds the kernels' indexing limits";
+    case FP8BSQ_ESCRATCH: return "the split needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }

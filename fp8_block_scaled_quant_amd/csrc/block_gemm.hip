@@ -18,6 +18,7 @@
 // result sits in lane l as column (l % 16), rows 4 * (l / 16) + 0..3.
 #include <atomic>
 
+#include "fp8bsq.h"
 #include "launch.h"
 #include "quant_common.h"
 
@@ -1103,6 +1104,51 @@ hipError_t launch_block_gemm_split(const uint8_t *a, const float *a_s, const uin
                                     counters);
   if (e != hipSuccess || !mx_kernel_used(k, a_s, a_s_pow2)) return e;
   return launch_ue8m0_guard(a_s, m, k, c, c_bf16, n, stream);
+}
+
+// Split-K scratch of launch_block_gemm_split_noalloc: one array per GPU,
+// living as long as the process.  A split's partials take tail * parts tiles
+// of 256 x 256 FP32 with tail * parts <= CUs, and its counters one word per
+// tail tile (tail <= CUs / 2), so 256 CUs need at most 512 B + 64 MiB.
+static_assert(FP8BSQ_SPLIT_SCRATCH_BYTES ==
+                  512 + (size_t)256 * kTileM * kTileN * sizeof(float),
+              "scratch size");
+static __device__ __align__(256) uint8_t scratch[FP8BSQ_SPLIT_SCRATCH_BYTES];
+
+// Device address of the current device's scratch, looked up on the first
+// call there (the array's name is a host-side stand-in, not that address).
+static hipError_t scratch_address(void **out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> address[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = address[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    address[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_block_gemm_split_noalloc(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                           const float *b_s, void *c, bool c_bf16, int64_t m,
+                                           int64_t n, int64_t k, hipStream_t stream, bool a_s_pow2,
+                                           bool *too_big) {
+  const size_t need = split_plan(m, n, k).bytes;
+  *too_big = need > FP8BSQ_SPLIT_SCRATCH_BYTES;
+  if (*too_big) return hipSuccess;
+  if (need == 0)   // no split pays: the unsplit launch, which uses no scratch
+    return launch_block_gemm(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, nullptr, a_s_pow2);
+  void *ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_block_gemm_split(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, a_s_pow2, ws,
+                                 FP8BSQ_SPLIT_SCRATCH_BYTES);
 }
 
 hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *b,

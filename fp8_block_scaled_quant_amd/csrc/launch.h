@@ -49,6 +49,14 @@ hipError_t launch_block_gemm_split(const uint8_t *a, const float *a_s, const uin
                                    int64_t k, hipStream_t stream, bool a_s_pow2, void *workspace,
                                    size_t workspace_bytes);
 
+// launch_block_gemm_split with the library's static per-device scratch
+// (FP8BSQ_SPLIT_SCRATCH_BYTES) as its workspace; *too_big is set, and nothing
+// queued, when the split needs more than that.
+hipError_t launch_block_gemm_split_noalloc(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                           const float *b_s, void *c, bool c_bf16, int64_t m,
+                                           int64_t n, int64_t k, hipStream_t stream, bool a_s_pow2,
+                                           bool *too_big);
+
 // Fused act_quant + decode GEMM (bf16 x [m, k], m small enough for
 // act_quant_gemm_fusable): C = Q(x) . B^T (+ bias); a_q / a_s receive
 // act_quant's codes and scales.

@@ -43,7 +43,8 @@ typedef enum {
   FP8BSQ_EUNSUPPORTED = 3, /* block_size != 128 */
   FP8BSQ_EALIGN = 4,       /* a pointer lacks the alignment stated for it */
   FP8BSQ_ELAUNCH = 5,      /* the HIP runtime reported an error for the launch */
-  FP8BSQ_ERANGE = 6        /* a size does not fit the kernels' 32-bit indexing limits */
+  FP8BSQ_ERANGE = 6,       /* a size does not fit the kernels' 32-bit indexing limits */
+  FP8BSQ_ESCRATCH = 7      /* the product needs more scratch than the static buffer holds */
 } fp8bsq_status;
 
 typedef enum { FP8BSQ_F32 = 0, FP8BSQ_BF16 = 1 } fp8bsq_dtype;
@@ -238,6 +239,29 @@ FP8BSQ_API int fp8_block_gemm_split(const uint8_t *a, const float *a_s, const ui
  * count; queues no work.
  */
 FP8BSQ_API size_t fp8_block_gemm_split_workspace(int64_t m, int64_t n, int64_t k);
+
+/*
+ * fp8_block_gemm_split_noalloc -- fp8_block_gemm_split without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same product, arguments (less workspace and workspace_bytes), layouts,
+ * bound and errors as fp8_block_gemm_split.  The split-K scratch (partial
+ * tiles and per-tile counters) lives in a static device array of
+ * FP8BSQ_SPLIT_SCRATCH_BYTES bytes inside the library, one per GPU, held until
+ * the process ends; its address is looked up once per device, on the first
+ * call there.  The call allocates nothing and clears the counters it uses
+ * itself (with a kernel, no memset).  A product whose split needs more than
+ * FP8BSQ_SPLIT_SCRATCH_BYTES (fp8_block_gemm_split_workspace(m, n, k) larger;
+ * not possible on a 256-CU device) returns FP8BSQ_ESCRATCH and queues nothing.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (other streams, other threads) race on it and must be ordered by
+ * the caller, or use fp8_block_gemm_split with separate workspaces.
+ */
+#define FP8BSQ_SPLIT_SCRATCH_BYTES ((size_t)67109376) /* 512 + 256 * 256 * 256 * 4: 64 MiB + 512 B */
+FP8BSQ_API int fp8_block_gemm_split_noalloc(const uint8_t *a, const float *a_s, const uint8_t *b,
+                                 const float *b_s, void *c, int c_dtype, int64_t m, int64_t n,
+                                 int64_t k, int scale_fmt, void *hip_stream);
 
 /*
  * fp8_act_quant_gemm -- a linear layer's forward product in one call:

@@ -51,13 +51,14 @@ def test_header_enums_match_binding():
     for name, val in [("FP8BSQ_OK", _lib.OK), ("FP8BSQ_EINVAL", _lib.EINVAL), ("FP8BSQ_ESHAPE", _lib.ESHAPE),
                       ("FP8BSQ_EUNSUPPORTED", _lib.EUNSUPPORTED), ("FP8BSQ_EALIGN", _lib.EALIGN),
                       ("FP8BSQ_ELAUNCH", _lib.ELAUNCH), ("FP8BSQ_ERANGE", _lib.ERANGE),
+                      ("FP8BSQ_ESCRATCH", _lib.ESCRATCH),
                       ("FP8BSQ_F32", _lib.F32), ("FP8BSQ_BF16", _lib.BF16),
                       ("FP8BSQ_SCALE_NONE", _lib.SCALE_NONE), ("FP8BSQ_SCALE_UE8M0", _lib.SCALE_UE8M0)]:
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
 
 
 def test_strerror_and_version(lib):
-    for st in range(7):
+    for st in range(8):
         assert lib.fp8bsq_strerror(st)
     assert lib.fp8bsq_strerror(99) == b"unknown status"
     assert re.match(rb"^\d+\.\d+\.\d+$", lib.fp8bsq_version())
@@ -118,6 +119,20 @@ def test_block_gemm_split_validation(lib):
     assert lib.fp8_block_gemm_split_workspace(0, 16, 128) == 0
     assert lib.fp8_block_gemm_split_workspace(16, 16, 100) == 0
     assert lib.fp8_block_gemm_split_workspace(1 << 40, 16, 128) == 0
+
+
+def test_block_gemm_split_noalloc_validation(lib):
+    f = lib.fp8_block_gemm_split_noalloc
+    assert f(None, P, P, P, P, 1, 16, 16, 128, 0, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, 16, 0, 128, 0, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 3, 16, 16, 128, 0, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, 16, 16, 128, 2, None) == _lib.EINVAL      # scale_fmt
+    assert f(P, P, P, P, P, 1, 16, 16, 100, 0, None) == _lib.ESHAPE
+    assert f(P + 8, P, P, P, P, 1, 16, 16, 128, 1, None) == _lib.EALIGN
+    assert f(P, P, P, P, P + 2, 1, 16, 16, 128, 1, None) == _lib.EALIGN
+    assert f(P, P, P, P, P, 1, 1 << 40, 16, 128, 0, None) == _lib.ERANGE
+    text = open(HEADER).read()
+    assert re.search(rf"#define FP8BSQ_SPLIT_SCRATCH_BYTES \(\(size_t\){_lib.SPLIT_SCRATCH_BYTES}\)", text)
 
 
 def test_weight_quant_validation(lib):
@@ -218,6 +233,19 @@ def test_dispatch_gemms(lib):
     assert ptrs[:7] == [a, a_s, b, b_s, c, S, P + 0x1000]
     assert lib.fp8_block_gemm_split(a, a_s, b, b_s, c, 0, 300, 700, 1024, 0, None, 5000, S) == _lib.OK
     assert st.last()[2][4:6] == [0, 0]                      # no workspace: zero bytes passed on
+
+
+def test_dispatch_split_noalloc(lib):
+    st = Stub(lib)
+    S = 0x7000
+    a, a_s, b, b_s, c = P, P + 0x100, P + 0x200, P + 0x300, P + 0x400
+    assert lib.fp8_block_gemm_split_noalloc(a, a_s, b, b_s, c, 1, 300, 700, 1024, 1, S) == _lib.OK
+    _, got, ints, ptrs = st.last()
+    assert got == "block_gemm_split_noalloc" and ints[:5] == [1, 300, 700, 1024, 1]
+    assert ptrs[:6] == [a, a_s, b, b_s, c, S]
+    n0 = st.last()[0]
+    assert lib.fp8_block_gemm_split_noalloc(a, a_s, b, b_s, c, 1, 777, 700, 1024, 0, S) == _lib.ESCRATCH
+    assert st.last()[0] == n0                                 # nothing launched
 
 
 def test_dispatch_act_quant_gemm(lib):
