@@ -368,10 +368,42 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](int kb, int cur) {
+    // MFMA q = 4 j + i of a K block; its rescale runs three MFMAs later (a ring
+    // of 4 partials).  With kMxA the rescale of a block's last three MFMAs runs
+    // at the top of the next block, behind that block's fragment reads (and
+    // after the tile's last block); the partials start at zero so that the
+    // first block of a tile adds nothing for a previous one.  (The generic
+    // kernel keeps it at the end of the block: carrying its row scales into the
+    // next block would spill.)
+    constexpr bool kDefer = kMxA;
+    f32x4 prt[4];
+    float sc[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      prt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[q][e] = 0.f;
+    }
+    float sb_prev = 0.f;
+    auto finish_block = [&]() {
+#pragma unroll
+      for (int qp = 29; qp < 32; ++qp) {
+        const int ip = qp % 4, jp = qp / 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[ip][jp][e] = __builtin_fmaf(prt[qp % 4][e], kMxA ? sb_prev : sc[ip][e], acc[ip][jp][e]);
+      }
+    };
+
+    // landed: stage cur is known to have landed for every wave (the first block
+    // of a persistent tile, whose transfers were waited for before the previous
+    // tile's output stores)
+    auto step = [&](int kb, int cur, bool landed) {
       const float sbv = bs_row[kb];   // scalar load, issued ahead of the wait below
-      wait_dma_all();
-      workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
+      if (!landed) {
+        wait_dma_all();
+        workgroup_barrier();   // stage cur landed for every wave; stage cur^1 no longer read
+      }
       if (dma_wave) {
         if (kb + 1 < kb_end) issue_a(kb + 1, cur ^ 1);
         // the table buffer of chunk c + 1 was last read in chunk c - 1
@@ -381,18 +413,6 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       // LDS results share one counter and the scalar one may return out of order,
       // so while it is outstanding every LDS wait would have to be a full drain.
       asm volatile("" ::"s"(sbv));
-      // fragment reads first: the first MFMA waits only for these
-      i32x8 af[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm + 16 * i + fr;
-        af[i] = frag_from_lds(&sm.a[cur][r * kBlock], fq, r);
-      }
-      auto read_b = [&](int j) {
-        const int r = wn + 16 * j + fr;
-        return frag_from_lds(&sm.b[cur][r * kBlock], fq, r);
-      };
-      i32x8 bcur = read_b(0), bnext;
       // kMxA (activation scales that are powers of two, act_quant's ue8m0): the
       // MFMA applies a_s of the A row a lane feeds (its E8M0 exponent, the fp32
       // exponent field), leaving the rescale a multiply by the wave-uniform b_s.
@@ -403,30 +423,56 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       const float *tab = &sm.tab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
       // table row r = wm + 16 i + x lies in 32-row block wm / 32 + i / 2, at row
       // 16 (i % 2) + x of it; the MFMA scale wants x = fr, the rescale x = 4 fq + e
+      auto tab_row = [&](int i) { return tab + (wm / 32 + i / 2) * 256 + 16 * (i % 2) * 4; };
+      // Reads in the order the first MFMAs use them -- the MFMA scales, B's first
+      // fragment, then A's fragments one by one -- so the first MFMA waits for
+      // three of them rather than all; the rescale's row scales come last.
+      uint32_t ew[4];   // the scale words; their exponent fields are taken after the reads go out
+      if (kMxA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ew[i] = __float_as_uint(tab_row(i)[fr * 4]);
+      }
+      auto read_b = [&](int j) {
+        const int r = wn + 16 * j + fr;
+        return frag_from_lds(&sm.b[cur][r * kBlock], fq, r);
+      };
+      i32x8 bcur = read_b(0), bnext;
+      __builtin_amdgcn_sched_barrier(0);
+      i32x8 af[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float *tb = tab + (wm / 32 + i / 2) * 256 + 16 * (i % 2) * 4;
-        if (kMxA) {
-          ea[i] = (int)((__float_as_uint(tb[fr * 4]) >> 23) & 0xFFu);
-        } else if (kTab) {
+        const int r = wm + 16 * i + fr;
+        af[i] = frag_from_lds(&sm.a[cur][r * kBlock], fq, r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (!kMxA) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sav[i][e] = tb[(4 * fq + e) * 4];
-        } else {
-          sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+        for (int i = 0; i < 4; ++i) {
+          if (kTab) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sav[i][e] = tab_row(i)[(4 * fq + e) * 4];
+          } else {
+            sav[i] = *(const f32x4 *)(&sm.as[cur][wm + 16 * i + 4 * fq]);
+          }
         }
       }
-      // MFMA q = 4 j + i; its rescale runs three MFMAs later (ring of 4 partials).
+      __builtin_amdgcn_sched_barrier(0);
+      if (kMxA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ea[i] = (int)((ew[i] >> 23) & 0xFFu);
+      }
+      // the previous block's last rescale, while these reads are in flight
+      if (kDefer) finish_block();
+      __builtin_amdgcn_sched_barrier(0);
       // The row scales a_s * b_s are formed at their first use (q - 3 < 4), so
       // their LDS reads never hold up the first MFMAs.
-      float sc[4][4];
-      f32x4 part[4];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j + 1 < 8) bnext = read_b(j + 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int q = 4 * j + i;
-          part[q % 4] = kMxA ? mfma_e4m3_16x16x128_mx(af[i], bcur, ea[i])
+          prt[q % 4] = kMxA ? mfma_e4m3_16x16x128_mx(af[i], bcur, ea[i])
                              : mfma_e4m3_16x16x128(af[i], bcur, f32x4{0.f, 0.f, 0.f, 0.f});
           // the next block's B, unconditionally so that no branch splits the
           // unrolled loop (the last block re-reads itself into the stage no one
@@ -440,19 +486,14 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
+              acc[ip][jp][e] = __builtin_fmaf(prt[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
         if (j + 1 < 8) bcur = bnext;
       }
-#pragma unroll
-      for (int qp = 29; qp < 32; ++qp) {
-        const int ip = qp % 4, jp = qp / 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[ip][jp][e] = __builtin_fmaf(part[qp % 4][e], kMxA ? sbv : sc[ip][e], acc[ip][jp][e]);
-      }
+      sb_prev = sbv;
+      if (!kDefer) finish_block();
     };
 
     if (!prologue_done) {
@@ -462,12 +503,17 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
       }
       issue_b(kb_begin, 0);
     }
+    const bool stage0_landed = prologue_done;
 #pragma nounroll
-    for (int kb = kb_begin; kb < kb_end; ++kb) step(kb, (kb - kb_begin) & 1);
+    for (int kb = kb_begin; kb < kb_end; ++kb) step(kb, (kb - kb_begin) & 1, kb == kb_begin && stage0_landed);
+    if (kDefer) finish_block();
     wait_dma_all();
 
-    // persistent: the next tile's first transfers (stage 0, table chunk 0) go
-    // out before this tile's output stores, once every wave is done with LDS
+    // persistent: once every wave is done with LDS, the next tile's first
+    // transfers (stage 0, table chunk 0) go out and are waited for, and only
+    // then this tile's output stores: the next tile's first block then starts
+    // without a wait, and its stores drain while that block computes (a wait
+    // for transfers issued after the stores would wait for them too)
     prologue_done = false;
     if (!kSplit && tile_it + (int)gridDim.x < tile_end) {
       workgroup_barrier();
@@ -479,6 +525,8 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
         if (kTab) issue_tab(0);
       }
       issue_b(0, 0);
+      wait_dma_all();
+      workgroup_barrier();
       prologue_done = true;
     }
 
