@@ -594,12 +594,21 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 // dominates the traffic).
 //
 // A workgroup owns 80 weight rows, one 16-row MFMA tile per compute wave
-// (waves 0-4), and all of them walk the same K blocks.  A sixth wave only
-// moves A: it DMAs each K block of A (16 kMT rows x 128 bytes, in whole-line
-// 16-byte pieces, with the XOR swizzle of the tiled kernel) and its kMT x 16
-// activation scales into an LDS ring of kDecodeSlots slots, kDecodeLead
+// (waves 0-4), and all of them walk the same K blocks.  A last wave only
+// moves A: it DMAs each K block of A (all its activation rows x 128 bytes, in
+// whole-line 16-byte pieces, with the XOR swizzle of the tiled kernel) and
+// their activation scales into an LDS ring of kDecodeSlots slots, kDecodeLead
 // blocks ahead, waiting on its own transfers only, and one barrier per K block
-// hands the ring on.  The weight streams from HBM per compute wave (below), so
+// hands the ring on.
+//
+// Above 32 activation rows (kSplitM = 2) each 16 weight rows get two compute
+// waves, one per half of the activation rows (two 16-row tiles each), ten
+// compute waves in all.  With one wave per weight tile, the five waves' MFMA
+// and rescale work sat unevenly on the four SIMDs (two waves on one of them)
+// and bounded every K block; the split spreads it (9% faster at M = 64,
+// outputs bit-identical).  Each wave of a pair fills its own copy of the
+// pair's weight rows: one ring shared through the K block's barrier, filled by
+// one wave, measured 7-10% slower.  The weight streams from HBM per compute wave (below), so
 // the only vector-memory transfers a compute wave waits on are its own weight
 // loads.  (A first design split K across four waves instead: every workgroup
 // then pulled all of A through fragment-shaped loads, and because a wave's
@@ -675,6 +684,7 @@ constexpr int kDecodeRows = 16 * kDecodeCompute;   // weight rows per workgroup
 constexpr int kDecodeLead = 6;                   // K blocks of A in flight ahead of use
 constexpr int kDecodeSlots = kDecodeLead + 1;   // LDS ring slots
 constexpr int kDecodeDepth = 6;                  // weight ring depth per compute wave (even)
+constexpr int kDecodeSplitDepth = 4;             // the same with the activation rows split over two waves
 
 template <int kMT>
 struct DecodeSlot {
@@ -694,18 +704,22 @@ struct DecodeSlot {
 // kTabKb K blocks' scales per row, loaded one chunk ahead in 16-byte pieces;
 // otherwise each K block's kRows scales travel in its ring slot, one 4-byte
 // transfer per row.
-template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false>
-__global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_kernel(
+template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false, int kSplitM = 1>
+__global__ __launch_bounds__(64 * (kDecodeCompute * kSplitM + 1)) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
     float *__restrict__ a_s_out = nullptr) {
-  static_assert(!kFuseQ || kMT == 1, "the fused path covers m <= kFusedMaxM");
-  constexpr int kRows = 16 * kMT;
+  static_assert(!kFuseQ || (kMT == 1 && kSplitM == 1), "the fused path covers m <= kFusedMaxM");
+  // kSplitM > 1: the activation rows are split over kSplitM compute waves per
+  // 16 weight rows, each taking kMT row tiles (wave w: weight rows 16 (w /
+  // kSplitM), activation tiles kMT (w % kSplitM) ..); kRows counts them all
+  constexpr int kCompute = kDecodeCompute * kSplitM;
+  constexpr int kRows = 16 * kMT * kSplitM;
   constexpr int kDmaPerBlock = kRows / 8 + (kTab ? 0 : 1);   // A row groups of 8 (+ the scales)
   // table: [32-row block][half][row][4 K blocks], as the DMA lanes lay it down
   constexpr int kTabRows = (kRows + 31) / 32 * 32;   // whole 32-row blocks (one DMA each)
-  __shared__ __attribute__((aligned(1024))) DecodeSlot<kMT> ring[kFuseQ ? 1 : kDecodeSlots];
+  __shared__ __attribute__((aligned(1024))) DecodeSlot<kMT * kSplitM> ring[kFuseQ ? 1 : kDecodeSlots];
   // fused: codes [m][k] (dynamic) and scales [kb][row] of all of x
   extern __shared__ __attribute__((aligned(16))) uint8_t aq[];
   __shared__ float as_t[kFuseQ ? kDecodeMaxKb : 1][kRows];
@@ -715,11 +729,16 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
   // of fragment-shaped loads); above that the waves' A-fragment reads already
   // load the LDS heavily, and the weight fragments stream into registers
   constexpr bool kBLds = kMT <= 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t bring[kBLds ? kDecodeCompute : 1][kBLds ? kDepth : 1]
+  // (one ring per compute wave: with the activation rows split over kSplitM
+  // waves, each wave of a group fills its own copy of the group's weight rows,
+  // which measured faster than one ring shared through the K block's barrier)
+  __shared__ __attribute__((aligned(1024))) uint8_t bring[kBLds ? kCompute : 1][kBLds ? kDepth : 1]
                                                          [kBLds ? 16 * kBlock : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool mover = !kFuseQ && wave == kDecodeCompute;
+  const bool mover = !kFuseQ && wave == kCompute;
+  const int wgroup = wave / kSplitM;            // the wave's 16 weight rows
+  const int mt0 = (wave % kSplitM) * kMT;       // its first activation row tile
   const int nkb = (int)(k / kBlock);
 
   // mover: lane p of row group g fills chunk slot p % 8 of row 8 g + p / 8;
@@ -734,7 +753,7 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
   const uint32_t s_off = (uint32_t)(min((int64_t)lane, m - 1) * nkb * 4);
   const uint32_t lds_ring = lds_addr(&ring[0]);
   auto issue = [&](int kb) {
-    const uint32_t slot = lds_ring + (uint32_t)((kb % kDecodeSlots) * sizeof(DecodeSlot<kMT>));
+    const uint32_t slot = lds_ring + (uint32_t)((kb % kDecodeSlots) * sizeof(DecodeSlot<kMT * kSplitM>));
 #pragma unroll
     for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
     if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + kRows * kBlock);
@@ -770,7 +789,7 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
     }
   };
 
-  const int64_t n0 = (int64_t)blockIdx.x * kDecodeRows + 16 * (mover ? 0 : wave);
+  const int64_t n0 = (int64_t)blockIdx.x * kDecodeRows + 16 * (mover ? 0 : wgroup);
   const int fr = lane & 15, fq = lane >> 4;
   const float *bs_row = b_s + min(n0 / kBlock, (n - 1) / kBlock) * nkb;
   // kBLds: each compute wave DMAs its own 16 weight rows of a K block (two
@@ -860,21 +879,22 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
       sb[buf] = bs_row[kbc];
       return;
     }
-    const DecodeSlot<kMT> &sl = ring[kb % kDecodeSlots];
+    const DecodeSlot<kMT * kSplitM> &sl = ring[kb % kDecodeSlots];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
-      const uint4 lo = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_lo]);
-      const uint4 hi = *(const uint4 *)(&sl.a[mt * 16 * kBlock + a_hi]);
+      const int tile = mt0 + mt;
+      const uint4 lo = *(const uint4 *)(&sl.a[tile * 16 * kBlock + a_lo]);
+      const uint4 hi = *(const uint4 *)(&sl.a[tile * 16 * kBlock + a_hi]);
       af[buf][mt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       if (kTab) {
         const float *tb = &stab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * mt + 4 * fq + e;
+          const int r = 16 * tile + 4 * fq + e;
           sa[buf][mt][e] = tb[(r >> 5) * 256 + (r & 31) * 4];
         }
       } else {
-        sa[buf][mt] = *(const f32x4 *)&sl.s[16 * mt + 4 * fq];
+        sa[buf][mt] = *(const f32x4 *)&sl.s[16 * tile + 4 * fq];
       }
     }
     sb[buf] = bs_row[min(kb, nkb - 1)];
@@ -959,7 +979,7 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t row = 16 * mt + 4 * fq + e;
+      const int64_t row = 16 * (mt0 + mt) + 4 * fq + e;
       if (row < m && col < n) store_out(c, kBf16Out, row * n + col, acc[mt][e] + bv);
     }
 }
@@ -1212,26 +1232,28 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   // the decode kernel's A and weight transfers use 32-bit lane offsets (from A's
   // base, and from each wave's first weight row)
   if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && 16 * k < ((int64_t)1 << 32)) {
-    const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * (kDecodeCompute + 1));
+    const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
-#define FP8BSQ_DECODE_T(MT, TAB)                                                                          \
-  do {                                                                                                     \
-    if (c_bf16)                                                                                            \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, kDecodeDepth, TAB>), grid, block, 0, stream, \
-                         a, a_s, b, b_s, c, m, n, k, bias);                                                \
-    else                                                                                                   \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, kDecodeDepth, TAB>), grid, block, 0,        \
-                         stream, a, a_s, b, b_s, c, m, n, k, bias);                                        \
+    // (MT, SPLIT, DEPTH): MT activation row tiles per compute wave, SPLIT
+    // compute waves per 16 weight rows, weight ring DEPTH
+#define FP8BSQ_DECODE_T(MT, SPLIT, DEPTH, TAB)                                                              \
+  do {                                                                                                       \
+    const dim3 block(64 * (kDecodeCompute * SPLIT + 1));                                                    \
+    if (c_bf16)                                                                                              \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, DEPTH, TAB, false, SPLIT>), grid, block, 0,    \
+                         stream, a, a_s, b, b_s, c, m, n, k, bias);                                          \
+    else                                                                                                     \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, DEPTH, TAB, false, SPLIT>), grid, block, 0,   \
+                         stream, a, a_s, b, b_s, c, m, n, k, bias);                                          \
   } while (0)
-#define FP8BSQ_DECODE(MT)                                                                                 \
-  do {                                                                                                     \
-    if (tab) FP8BSQ_DECODE_T(MT, true); else FP8BSQ_DECODE_T(MT, false);                                 \
+#define FP8BSQ_DECODE(MT, SPLIT, DEPTH)                                                                     \
+  do {                                                                                                       \
+    if (tab) FP8BSQ_DECODE_T(MT, SPLIT, DEPTH, true); else FP8BSQ_DECODE_T(MT, SPLIT, DEPTH, false);       \
   } while (0)
     switch ((m + 15) / 16) {
-      case 1: FP8BSQ_DECODE(1); break;
-      case 2: FP8BSQ_DECODE(2); break;
-      case 3: FP8BSQ_DECODE(3); break;
-      default: FP8BSQ_DECODE(4); break;
+      case 1: FP8BSQ_DECODE(1, 1, kDecodeDepth); break;
+      case 2: FP8BSQ_DECODE(2, 1, kDecodeDepth); break;
+      default: FP8BSQ_DECODE(2, 2, kDecodeSplitDepth); break;
     }
 #undef FP8BSQ_DECODE
 #undef FP8BSQ_DECODE_T
