@@ -597,8 +597,8 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 // (waves 0-4), and all of them walk the same K blocks.  A last wave only
 // moves A: it DMAs each K block of A (all its activation rows x 128 bytes, in
 // whole-line 16-byte pieces, with the XOR swizzle of the tiled kernel) and
-// their activation scales into an LDS ring of kDecodeSlots slots, kDecodeLead
-// blocks ahead, waiting on its own transfers only, and one barrier per K block
+// their activation scales into an LDS ring, kLead blocks ahead (kLead + 1
+// slots), waiting on its own transfers only, and one barrier per K block
 // hands the ring on.
 //
 // Above 32 activation rows (kSplitM = 2) each 16 weight rows get two compute
@@ -681,8 +681,8 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
 
 constexpr int kDecodeCompute = 5;                // compute waves per workgroup (plus the mover)
 constexpr int kDecodeRows = 16 * kDecodeCompute;   // weight rows per workgroup
-constexpr int kDecodeLead = 6;                   // K blocks of A in flight ahead of use
-constexpr int kDecodeSlots = kDecodeLead + 1;   // LDS ring slots
+constexpr int kDecodeLead = 6;                   // K blocks of A in flight ahead of use (ring: one more slot)
+constexpr int kDecodeSplitLead = 6;              // the same with the activation rows split over two waves
 constexpr int kDecodeDepth = 6;                  // weight ring depth per compute wave (even)
 constexpr int kDecodeSplitDepth = 4;             // the same with the activation rows split over two waves
 
@@ -716,10 +716,12 @@ __global__ __launch_bounds__(64 * (kDecodeCompute * kSplitM + 1)) void block_gem
   // kSplitM), activation tiles kMT (w % kSplitM) ..); kRows counts them all
   constexpr int kCompute = kDecodeCompute * kSplitM;
   constexpr int kRows = 16 * kMT * kSplitM;
+  constexpr int kLead = kSplitM > 1 ? kDecodeSplitLead : kDecodeLead;   // A blocks in flight ahead
+  constexpr int kSlots = kLead + 1;
   constexpr int kDmaPerBlock = kRows / 8 + (kTab ? 0 : 1);   // A row groups of 8 (+ the scales)
   // table: [32-row block][half][row][4 K blocks], as the DMA lanes lay it down
   constexpr int kTabRows = (kRows + 31) / 32 * 32;   // whole 32-row blocks (one DMA each)
-  __shared__ __attribute__((aligned(1024))) DecodeSlot<kMT * kSplitM> ring[kFuseQ ? 1 : kDecodeSlots];
+  __shared__ __attribute__((aligned(1024))) DecodeSlot<kMT * kSplitM> ring[kFuseQ ? 1 : kSlots];
   // fused: codes [m][k] (dynamic) and scales [kb][row] of all of x
   extern __shared__ __attribute__((aligned(16))) uint8_t aq[];
   __shared__ float as_t[kFuseQ ? kDecodeMaxKb : 1][kRows];
@@ -753,7 +755,7 @@ __global__ __launch_bounds__(64 * (kDecodeCompute * kSplitM + 1)) void block_gem
   const uint32_t s_off = (uint32_t)(min((int64_t)lane, m - 1) * nkb * 4);
   const uint32_t lds_ring = lds_addr(&ring[0]);
   auto issue = [&](int kb) {
-    const uint32_t slot = lds_ring + (uint32_t)((kb % kDecodeSlots) * sizeof(DecodeSlot<kMT * kSplitM>));
+    const uint32_t slot = lds_ring + (uint32_t)((kb % kSlots) * sizeof(DecodeSlot<kMT * kSplitM>));
 #pragma unroll
     for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
     if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + kRows * kBlock);
@@ -777,7 +779,7 @@ __global__ __launch_bounds__(64 * (kDecodeCompute * kSplitM + 1)) void block_gem
   };
   // wait until a K block's transfers have landed, given how many blocks were
   // issued after it (transfers complete in issue order)
-  static_assert(kDecodeLead == 6 && 5 * kDmaPerBlock < 64, "one vmcnt case per block behind");
+  static_assert(kLead <= 6 && 5 * kDmaPerBlock < 64, "one vmcnt case per block behind");
   auto wait_block = [&](int behind) {
     switch (behind) {
       case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * kDmaPerBlock) : "memory"); break;
@@ -839,17 +841,17 @@ __global__ __launch_bounds__(64 * (kDecodeCompute * kSplitM + 1)) void block_gem
     // the compute waves read block kb + 1 while they compute kb, so by the
     // barrier that ends block kb, block kb + 2 must have landed
     if (kTab) issue_tab(0);
-    for (int kb = 0; kb < kDecodeLead && kb < nkb; ++kb) issue(kb);
-    wait_block(min(kDecodeLead, nkb) - 1 - min(1, nkb - 1));
+    for (int kb = 0; kb < kLead && kb < nkb; ++kb) issue(kb);
+    wait_block(min(kLead, nkb) - 1 - min(1, nkb - 1));
     workgroup_barrier();
     for (int kb = 0; kb < nkb; ++kb) {
       // the slot of kb + lead was last read during block kb - 2
-      if (kb + kDecodeLead < nkb) issue(kb + kDecodeLead);
+      if (kb + kLead < nkb) issue(kb + kLead);
       // chunk c + 1 into the buffer chunk c - 1 used (last read during block
       // kb - 2); it is older than block kb + 7's transfers, which are waited
       // for (two blocks ahead of their use) before its first read
       if (kTab && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
-      if (kb + 2 < nkb) wait_block(min(kb + kDecodeLead, nkb - 1) - (kb + 2));
+      if (kb + 2 < nkb) wait_block(min(kb + kLead, nkb - 1) - (kb + 2));
       workgroup_barrier();
     }
     wait_dma_all();
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(64 * (kDecodeCompute * kSplitM + 1)) void block_gem
       sb[buf] = bs_row[kbc];
       return;
     }
-    const DecodeSlot<kMT * kSplitM> &sl = ring[kb % kDecodeSlots];
+    const DecodeSlot<kMT * kSplitM> &sl = ring[kb % kSlots];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
       const int tile = mt0 + mt;

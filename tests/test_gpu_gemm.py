@@ -5,7 +5,8 @@ plus one bf16 ulp of C for BF16 output; NaN/Inf always fail.
 
 Cases: the tiny workload (fp32 activations [16, 512] quantized by the GPU
 act_quant, weights [256, 512], fp32 out); the decode workloads (M = 1, 8, 32,
-64, N = 18432, K = 7168, bf16 out), checked on every element; both prefill
+64, and 33 and 48 for the kernel that splits the activation rows over two
+waves; N = 18432, K = 7168, bf16 out), checked on every element; both prefill
 shapes at full size (M = 8192) checked on sampled rows (first, last and 512
 random rows, every column); ragged shapes with partial tiles in M and N.
 """
@@ -49,7 +50,7 @@ def test_tiny_workload_fp32_out():
     _assert_close(got, a, a_s, d["w"], d["w_s"], "f32", label="tiny")
 
 
-@pytest.mark.parametrize("m", [1, 8, 32, 64])
+@pytest.mark.parametrize("m", [1, 8, 32, 33, 48, 64])
 def test_decode_workloads(m):
     d = gen.decode_gemm(m)
     G.announce(f"gemm decode M={m} N=18432 K=7168 bf16")
