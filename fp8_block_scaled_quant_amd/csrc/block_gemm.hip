@@ -1066,53 +1066,39 @@ __global__ void zero_u32_kernel(uint32_t *p, int n) {
 // E8M0 exponent field of its fp32 bits: a row of a_s [m, nkb] holding any
 // value that is not a positive normal power of two (bits other than e << 23,
 // 1 <= e <= 254) gets NaN in every column of its C row.  Runs after the GEMM
-// on the same stream.  64 rows per workgroup, four lanes per row.
-constexpr int kGuardRows = 64;
+// on the same stream.  One lane per 16 bytes (four scales) of a_s, which the
+// MX-scaled kernel's preconditions (nkb % 4 == 0, 16-byte aligned a_s) keep
+// inside one row: a single load per lane when every scale is good, and a lane
+// that finds a stray scale fills its row with NaN itself.
 template <bool kBf16Out>
-__global__ __launch_bounds__(256) void ue8m0_guard_kernel(const float *__restrict__ a_s, int64_t m,
-                                                          int nkb, void *__restrict__ c, int64_t n) {
-  __shared__ uint32_t bad[kGuardRows];
-  __shared__ int any_bad;
-  const int t = threadIdx.x;
-  if (t < kGuardRows) bad[t] = 0u;
-  if (t == 0) any_bad = 0;
-  __syncthreads();
-  const int64_t row = (int64_t)blockIdx.x * kGuardRows + t / 4;
-  if (row < m) {
-    const uint32_t *r = (const uint32_t *)a_s + row * nkb;
-    uint32_t stray = 0u, low = 0xFFFFFFFFu;
-    for (int j = t % 4; j < nkb; j += 4) {
-      const uint32_t v = r[j];
-      stray |= v & 0x807FFFFFu;   // sign or mantissa bits
-      low = v < low ? v : low;    // zero or subnormal exponent
-    }
-    if (stray != 0u || low < 0x00800000u) {
-      bad[t / 4] = 1u;
-      any_bad = 1;
-    }
-  }
-  __syncthreads();
-  if (!any_bad) return;
-  for (int i = 0; i < kGuardRows; ++i) {
-    const int64_t rr = (int64_t)blockIdx.x * kGuardRows + i;
-    if (rr >= m || !bad[i]) continue;
-    for (int64_t j = t; j < n; j += 256) {
-      if (kBf16Out)
-        ((uint16_t *)c)[rr * n + j] = 0x7FC0u;
-      else
-        ((uint32_t *)c)[rr * n + j] = 0x7FC00000u;
-    }
+__global__ __launch_bounds__(256) void ue8m0_guard_kernel(const u32x4 *__restrict__ a_s4, int64_t nvec,
+                                                          int vec_per_row, void *__restrict__ c, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nvec) return;
+  const u32x4 v = a_s4[i];
+  const uint32_t stray = (v.x | v.y | v.z | v.w) & 0x807FFFFFu;   // sign or mantissa bits
+  const uint32_t lo = min(min(v.x, v.y), min(v.z, v.w));            // zero or subnormal exponent
+  if (stray == 0u && lo >= 0x00800000u) return;
+  const int64_t row = i / vec_per_row;
+  for (int64_t j = 0; j < n; ++j) {
+    if (kBf16Out)
+      ((uint16_t *)c)[row * n + j] = 0x7FC0u;
+    else
+      ((uint32_t *)c)[row * n + j] = 0x7FC00000u;
   }
 }
 
 static hipError_t launch_ue8m0_guard(const float *a_s, int64_t m, int64_t k, void *c, bool c_bf16,
                                      int64_t n, hipStream_t stream) {
-  const dim3 grid((unsigned)((m + kGuardRows - 1) / kGuardRows)), block(256);
-  const int nkb = (int)(k / kBlock);
+  const int vec_per_row = (int)(k / kBlock / 4);
+  const int64_t nvec = m * vec_per_row;
+  const dim3 grid((unsigned)((nvec + 255) / 256)), block(256);
   if (c_bf16)
-    hipLaunchKernelGGL(ue8m0_guard_kernel<true>, grid, block, 0, stream, a_s, m, nkb, c, n);
+    hipLaunchKernelGGL(ue8m0_guard_kernel<true>, grid, block, 0, stream, (const u32x4 *)a_s, nvec, vec_per_row,
+                       c, n);
   else
-    hipLaunchKernelGGL(ue8m0_guard_kernel<false>, grid, block, 0, stream, a_s, m, nkb, c, n);
+    hipLaunchKernelGGL(ue8m0_guard_kernel<false>, grid, block, 0, stream, (const u32x4 *)a_s, nvec,
+                       vec_per_row, c, n);
   return hipGetLastError();
 }
 
