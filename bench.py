@@ -39,7 +39,7 @@ reads for a copy of known size), read from profiles/block_gemm_prefill_traffic.j
 it is reported as null when the GEMM source has changed since those counters
 were taken.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-configs] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--no-configs] [--no-cpu]
        python bench.py --profile-workload NAME [--iters N]   (one kernel, for rocprofv3)
        python bench.py --calibrate-copy                      (copy of known size, for rocprofv3)
 """
@@ -104,7 +104,7 @@ def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--cpu-rows", type=int, default=6144,
                    help="activation rows in the CPU oracle sample of the step (0 skips it)")
     p.add_argument("--no-cpu", action="store_true", help="skip every CPU oracle timing")
@@ -356,7 +356,7 @@ def bench_configs(args, stream):
     from inputs import gen
 
     dev = torch.device("cuda:0")
-    reps, warm = args.config_reps, 5
+    reps, warm = args.config_reps, 20   # ~20 launches for the clock to settle after host-side work
     cpu = not args.no_cpu
     recs = {}
 
