@@ -94,7 +94,7 @@ def test_python_binding():
     (2, 300, 1024, "f32"),       # one kernel, ragged N
     (9, 500, 640, "bf16"),       # decode GEMM after act_quant
     (100, 384, 512, "f32"),      # tiled GEMM
-    (40, 700, 1024, "bf16"),     # decode GEMM, weight fragments through registers (M > 32)
+    (40, 700, 1024, "bf16"),     # wide decode kernel (M > 32)
     (3, 256, 20608, "bf16"),     # long K with K/128 = 161: no scale table
 ])
 def test_bias_in_epilogue(m, n, k, out):

@@ -4,9 +4,10 @@ Bound (per element): |gpu - C| <= 1e-3 * sum_k |a_k b_k| for FP32 output,
 plus one bf16 ulp of C for BF16 output; NaN/Inf always fail.
 
 Cases: the tiny workload (fp32 activations [16, 512] quantized by the GPU
-act_quant, weights [256, 512], fp32 out); the decode workloads (M = 1, 8, 32,
-64, and 33 and 48 for the kernel that splits the activation rows over two
-waves; N = 18432, K = 7168, bf16 out), checked on every element; both prefill
+act_quant, weights [256, 512], fp32 out); the decode workloads (M = 1, 8, 32
+through the decode kernel, and 33, 48 and 64 through the wide kernel, whose
+waves each run one activation tile against five weight tiles; N = 18432,
+K = 7168, bf16 out), checked on every element; both prefill
 shapes at full size (M = 8192) checked on sampled rows (first, last and 512
 random rows, every column); ragged shapes with partial tiles in M and N.
 """
@@ -73,7 +74,8 @@ def test_prefill_workloads_sampled_rows(shape):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (17, 200, 256), (33, 130, 384), (64, 129, 128),
                                    (100, 300, 1024), (130, 64, 640), (257, 385, 512),
-                                   (40, 100, 21504), (5, 70, 20608), (20, 300, 1536)])
+                                   (40, 100, 21504), (5, 70, 20608), (20, 300, 1536), (49, 81, 2048),
+                                   (56, 18440, 512)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_ragged_shapes(m, n, k, out):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
