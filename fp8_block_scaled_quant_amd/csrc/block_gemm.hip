@@ -933,13 +933,12 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
 // tiles) and all of A's row tiles (kAT = 3 or 4); compute wave w owns A's row
 // tile w and runs it against all five weight tiles, so each K block a wave
 // reads one A fragment and five weight fragments, and the MFMA and rescale
-// work sits evenly on the four SIMDs.  One mover wave DMAs each K block's A
-// rows, its 80 weight rows and (without the table) the rows' scales into a
-// kWideSlots-slot LDS ring, kWideLead blocks ahead, waiting on its own
-// transfers only; one barrier per K block hands the ring on, as in the decode
-// kernel.  (The lead is bounded by the wait counter: a block is 2 kAT + 10
-// transfers, and the mover waits with up to kWideLead - 2 younger blocks in
-// flight.)  Against two compute waves per weight tile, each DMAing its own
+// work sits evenly on the four SIMDs.  Two mover waves fill a kWideSlots-slot
+// LDS ring kWideLead blocks ahead: one DMAs each K block's A rows and (without
+// the table) their scales, the other its 80 weight rows.  Each waits on its
+// own transfers only, and one barrier per K block hands the ring on, as in the
+// decode kernel.  (One mover for both measured 1-3% slower.)  Against two
+// compute waves per weight tile, each DMAing its own
 // copy of the tile's rows, this measured 7-11% faster at M = 33-64 with
 // bit-identical outputs (each output element sees the same FMAs in the same
 // order); at M <= 32 it measured no faster than the decode kernel, and at
@@ -958,19 +957,20 @@ struct WideSlot {
 };
 
 template <bool kBf16Out, int kAT, bool kTab>
-__global__ __launch_bounds__(64 * (kAT + 1)) void block_gemm_decode_wide_kernel(
+__global__ __launch_bounds__(64 * (kAT + 2)) void block_gemm_decode_wide_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias) {
   constexpr int kRows = 16 * kAT;
-  constexpr int kDma = kRows / 8 + kWideRows / 8 + (kTab ? 0 : 1);   // transfers per K block
-  static_assert((kWideLead - 2) * kDma < 64, "the wait counter's range");
+  // transfers per K block of the A mover and of the weight mover
+  constexpr int kDmaA = kRows / 8 + (kTab ? 0 : 1), kDmaB = kWideRows / 8;
+  static_assert((kWideLead - 2) * kDmaB < 64 && (kWideLead - 2) * kDmaA < 64, "the wait counter's range");
   constexpr int kTabRows = (kRows + 31) / 32 * 32;
   __shared__ __attribute__((aligned(1024))) WideSlot<kAT> ring[kWideSlots];
   __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool mover = wave == kAT;
+  const bool mover = wave >= kAT, bmover = wave == kAT + 1;
   const int nkb = (int)(k / kBlock);
   const int64_t n0 = (int64_t)blockIdx.x * kWideRows;
 
@@ -995,12 +995,15 @@ __global__ __launch_bounds__(64 * (kAT + 1)) void block_gemm_decode_wide_kernel(
     const uint32_t lds_ring = lds_addr(&ring[0]);
     auto issue = [&](int kb) {
       const uint32_t slot = lds_ring + (uint32_t)((kb % kWideSlots) * sizeof(WideSlot<kAT>));
+      if (!bmover) {
 #pragma unroll
-      for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
+        for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
+        if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + (kRows + kWideRows) * kBlock);
+      } else {
 #pragma unroll
-      for (int g = 0; g < kWideRows / 8; ++g)
-        lds_dma16(b_base + (int64_t)kb * kBlock, b_off[g], slot + kRows * kBlock + g * 1024);
-      if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + (kRows + kWideRows) * kBlock);
+        for (int g = 0; g < kWideRows / 8; ++g)
+          lds_dma16(b_base + (int64_t)kb * kBlock, b_off[g], slot + kRows * kBlock + g * 1024);
+      }
     };
     // table chunk c into buffer c & 1, as in the decode kernel
     const int trow = lane & 31, thalf = lane >> 5;
@@ -1017,18 +1020,28 @@ __global__ __launch_bounds__(64 * (kAT + 1)) void block_gemm_decode_wide_kernel(
         if (32 * i + trow < kRows)
           lds_dma16(a_s, t_off[i] + piece, lds_tab + (ch & 1) * (kTabRows * kTabKb * 4) + i * 1024);
     };
-    auto wait_block = [&](int behind) {   // a block's transfers landed, `behind` younger blocks issued
-      switch (behind) {
-        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * kDma) : "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDma) : "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kDma) : "memory"); break;
-        default: wait_dma_all(); break;
+    // a block's transfers landed, `behind` younger blocks issued (the A
+    // mover's table chunks only make its waits stricter)
+    auto wait_block = [&](int behind) {
+#define FP8BSQ_WAIT_BEHIND(D)                                                     \
+  switch (behind) {                                                               \
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * (D)) : "memory"); break; \
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (D)) : "memory"); break; \
+    case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (D)) : "memory"); break; \
+    case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (D)) : "memory"); break; \
+    default: wait_dma_all(); break;                                               \
+  }
+      if (bmover) {
+        FP8BSQ_WAIT_BEHIND(kDmaB)
+      } else {
+        FP8BSQ_WAIT_BEHIND(kDmaA)
       }
+#undef FP8BSQ_WAIT_BEHIND
     };
-    static_assert(kWideLead - 2 <= 3, "one wait case per block behind");
+    static_assert(kWideLead - 2 <= 4, "one wait case per block behind");
     // the compute waves read block kb + 1 while they compute kb, so by the
     // barrier that ends block kb, block kb + 2 must have landed
-    if (kTab) issue_tab(0);
+    if (kTab && !bmover) issue_tab(0);
     for (int kb = 0; kb < kWideLead && kb < nkb; ++kb) issue(kb);
     wait_block(min(kWideLead, nkb) - 1 - min(1, nkb - 1));
     workgroup_barrier();
@@ -1037,7 +1050,7 @@ __global__ __launch_bounds__(64 * (kAT + 1)) void block_gemm_decode_wide_kernel(
       if (kb + kWideLead < nkb) issue(kb + kWideLead);
       // table chunk c + 1 into the buffer chunk c - 1 used (last read during
       // block kb - 2); older than the transfers waited for below
-      if (kTab && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
+      if (kTab && !bmover && kb % kTabKb == 0 && kb + kTabKb < nkb) issue_tab(kb / kTabKb + 1);
       if (kb + 2 < nkb) wait_block(min(kb + kWideLead, nkb - 1) - (kb + 2));
       workgroup_barrier();
     }
@@ -1374,7 +1387,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   } while (0)
 #define FP8BSQ_WIDE_T(AT, TAB)                                                                              \
   do {                                                                                                       \
-    const dim3 block(64 * (AT + 1));                                                                         \
+    const dim3 block(64 * (AT + 2));                                                                         \
     if (c_bf16)                                                                                              \
       hipLaunchKernelGGL((block_gemm_decode_wide_kernel<true, AT, TAB>), grid, block, 0, stream, a, a_s, b,  \
                          b_s, c, m, n, k, bias);                                                             \
