@@ -938,11 +938,10 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
 // the table) their scales, the other its 80 weight rows.  Each waits on its
 // own transfers only, and one barrier per K block hands the ring on, as in the
 // decode kernel.  (One mover for both measured 1-3% slower.)  Against two
-// compute waves per weight tile, each DMAing its own
-// copy of the tile's rows, this measured 7-11% faster at M = 33-64 with
-// bit-identical outputs (each output element sees the same FMAs in the same
-// order); at M <= 32 it measured no faster than the decode kernel, and at
-// M <= 16 2% slower.
+// compute waves per weight tile, each DMAing its own copy of the tile's rows,
+// this measured 7-11% faster at M = 33-64 with bit-identical outputs (each
+// output element sees the same FMAs in the same order); at M <= 32 it
+// measured no faster than the decode kernel, and at M <= 16 2% slower.
 // ---------------------------------------------------------------------------
 constexpr int kWideTiles = 5;                    // weight tiles per workgroup
 constexpr int kWideRows = 16 * kWideTiles;       // weight rows per workgroup (as kDecodeRows)
