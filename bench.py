@@ -109,7 +109,7 @@ def parse(argv=None):
                    help="activation rows in the CPU oracle sample of the step (0 skips it)")
     p.add_argument("--no-cpu", action="store_true", help="skip every CPU oracle timing")
     p.add_argument("--no-configs", action="store_true", help="time the step only")
-    p.add_argument("--config-reps", type=int, default=30,
+    p.add_argument("--config-reps", type=int, default=50,
                    help="timed launches per bandwidth-bound workload")
     p.add_argument("--prefill-rows", type=int, default=128,
                    help="activation rows in the CPU oracle sample of each prefill GEMM")
@@ -331,9 +331,13 @@ def blas_info():
 
 
 def hbm_record(us, nbytes, extra=None):
+    """Rate and HBM fraction of the mean launch time `us` (and of the median,
+    when `extra` holds "median_us")."""
     gbs = nbytes / (us * 1e-6) / 1e9
     rec = {"us": us, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": nbytes}
     rec.update(extra or {})
+    if "median_us" in rec:
+        rec["frac_hbm_median"] = nbytes / (rec["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS
     return rec
 
 
@@ -473,7 +477,8 @@ def bench_configs(args, stream):
         flop = 2 * M * n * k
         tf = flop / (gm[0] * 1e-6) / 1e12
         rec = {"workload": f"prefill GEMM {M}x{n}x{k}, ue8m0 activation scales, bf16 out",
-               "us": gm[0], "median_us": gm[1], "TFLOP/s": tf, "frac_mfma": tf / PEAK_FP8_TFLOPS, "flop": flop,
+               "us": gm[0], "median_us": gm[1], "TFLOP/s": tf, "frac_mfma": tf / PEAK_FP8_TFLOPS,
+               "frac_mfma_median": flop / (gm[1] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, "flop": flop,
                "act_quant_us": aq[0], "act_quant_bytes": act_quant_bytes(M, k)}
         if cpu and args.prefill_rows > 0:
             rows = args.prefill_rows
@@ -571,9 +576,11 @@ def main(argv=None):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    aq_ms = float(np.mean([ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.steps)]))
-    dq_ms = float(np.mean([ev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]))
-    gm_ms = float(np.mean([ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
+    aq_t = [ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.steps)]
+    dq_t = [ev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]
+    gm_t = [ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]
+    aq_ms, dq_ms, gm_ms = (float(np.mean(t)) for t in (aq_t, dq_t, gm_t))
+    aq_med, dq_med, gm_med = (float(np.median(t)) for t in (aq_t, dq_t, gm_t))
     ev.close()
     ms_per_step = elapsed * 1e3 / args.steps
 
@@ -610,11 +617,17 @@ def main(argv=None):
         },
         "kernels": {
             "act_quant": {"us": aq_ms * 1e3, "GB/s": aq_gbs, "frac_hbm": aq_gbs / PEAK_HBM_GBS,
+                          "median_us": aq_med * 1e3,
+                          "frac_hbm_median": ACT_QUANT_BYTES / (aq_med * 1e-3) / 1e9 / PEAK_HBM_GBS,
                           "bytes": ACT_QUANT_BYTES},
             "weight_dequant": {"us": dq_ms * 1e3, "GB/s": dq_gbs, "frac_hbm": dq_gbs / PEAK_HBM_GBS,
+                               "median_us": dq_med * 1e3,
+                               "frac_hbm_median": DEQUANT_BYTES / (dq_med * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                "bytes": DEQUANT_BYTES},
             "block_gemm": {"us": gm_ms * 1e3, "TFLOP/s": gemm_tflops,
-                           "frac_mfma": gemm_tflops / PEAK_FP8_TFLOPS, "flop": GEMM_FLOP},
+                           "frac_mfma": gemm_tflops / PEAK_FP8_TFLOPS, "median_us": gm_med * 1e3,
+                           "frac_mfma_median": GEMM_FLOP / (gm_med * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                           "flop": GEMM_FLOP},
         },
         "cpu_baseline": None,
     }
