@@ -119,7 +119,7 @@ def weight_dequant(x: torch.Tensor, s: torch.Tensor, block_size: int = 128,
 def weight_quant(w: torch.Tensor, block_size: int = 128, scale_fmt=None):
     """Quantize a 2-D weight per block_size x block_size tile.
 
-    ``w`` is a contiguous bf16 or fp32 CUDA tensor [M, N] (any M, N >= 1).
+    ``w`` is a contiguous bf16 or fp32 CUDA tensor [M, N] (any M, N >= 0).
     Returns ``y`` (float8_e4m3fn [M, N]) and ``s`` (float32
     [ceil(M/bs), ceil(N/bs)]), the operands ``weight_dequant`` and ``fp8_gemm``
     take.
@@ -165,9 +165,9 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Ten
     k = a.shape[-1]
     if b.dim() != 2 or b.shape[1] != k:
         raise ValueError("b must be [N, K] with A's K")
-    if k % 128 != 0:
-        raise ValueError("K must be a multiple of 128")
-    m = a.numel() // k if k else 0
+    if k <= 0 or k % 128 != 0:
+        raise ValueError("K must be a positive multiple of 128")
+    m = a.numel() // k
     n = b.shape[0]
     if tuple(a_s.shape) != tuple(a.shape[:-1]) + (k // 128,):
         raise ValueError("a_s must be a.shape[:-1] + (K/128,)")
@@ -211,8 +211,8 @@ def act_quant_gemm(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, scale_fm
     if b_s.dtype != torch.float32:
         raise TypeError("scales must be float32")
     k = x.shape[-1]
-    if k % 128 != 0:
-        raise ValueError("K must be a multiple of 128")
+    if k <= 0 or k % 128 != 0:
+        raise ValueError("K must be a positive multiple of 128")
     if b.dim() != 2 or b.shape[1] != k:
         raise ValueError("b must be [N, K] with x's K")
     n = b.shape[0]
@@ -220,11 +220,11 @@ def act_quant_gemm(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, scale_fm
         raise ValueError("b_s must be [ceil(N/128), K/128]")
     if bias is not None and (bias.dtype != out_dtype or tuple(bias.shape) != (n,)):
         raise ValueError(f"bias must be [{n}] of the output dtype {out_dtype}")
-    m = x.numel() // k if k else 0
+    m = x.numel() // k
     y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     s = torch.empty(x.shape[:-1] + (k // 128,), dtype=torch.float32, device=x.device)
     c = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=out_dtype, device=x.device)
-    if m and n:
+    if m:   # with n = 0 the library still writes y and s
         _lib.check(_lib.lib().fp8_act_quant_gemm(
             ctypes.c_void_p(x.data_ptr()), _DTYPE[x.dtype], _SCALE_FMT[scale_fmt],
             ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(b_s.data_ptr()),

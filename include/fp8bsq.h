@@ -17,6 +17,10 @@
  *  - The return value is FP8BSQ_OK or an fp8bsq_status code.  Arguments are
  *    validated before any HIP call; on a validation error nothing is queued.
  *    FP8BSQ_ELAUNCH reports an error from the HIP runtime after the launch.
+ *  - Empty inputs: a call whose outputs have no elements (a row or column
+ *    count of 0) passes the enum and shape checks, then returns FP8BSQ_OK
+ *    without queuing anything or reading its pointers, which may be NULL.  A
+ *    negative size is FP8BSQ_EINVAL, and so is k = 0 for a product.
  *  - Inputs must be finite.  NaN/Inf inputs or scales give unspecified (but
  *    memory-safe) outputs.
  *  - block_size is an argument because the format makes it configurable; only
@@ -38,7 +42,7 @@ extern "C" {
 
 typedef enum {
   FP8BSQ_OK = 0,
-  FP8BSQ_EINVAL = 1,       /* null pointer, dimension <= 0, unknown enum value */
+  FP8BSQ_EINVAL = 1,       /* null pointer, negative dimension (or k = 0 for a product), unknown enum */
   FP8BSQ_ESHAPE = 2,       /* a dimension that must be a multiple of block_size is not */
   FP8BSQ_EUNSUPPORTED = 3, /* block_size != 128 */
   FP8BSQ_EALIGN = 4,       /* a pointer lacks the alignment stated for it */
@@ -66,7 +70,8 @@ typedef enum {
  *
  *   x          [rows, k] activations, dtype x_dtype (FP8BSQ_F32 or FP8BSQ_BF16),
  *              16-byte aligned.
- *   rows, k    rows >= 1, k >= 1 and k % block_size == 0 (else FP8BSQ_ESHAPE).
+ *   rows, k    rows >= 0, k >= 0 and k % block_size == 0 (else FP8BSQ_ESHAPE);
+ *              either 0: nothing to do.
  *   scale_fmt  FP8BSQ_SCALE_NONE or FP8BSQ_SCALE_UE8M0 (smallest power of two
  *              >= fl32(amax/448)).
  *   y          [rows, k] E4M3 codes out, 8-byte aligned:
@@ -90,7 +95,7 @@ FP8BSQ_API int fp8_act_quant(const void *x, int x_dtype, int64_t rows, int64_t k
  *   x        [m, n] E4M3 codes (m weight rows, n columns), any alignment.
  *   s        [ceil(m / block_size), ceil(n / block_size)] FP32 scales
  *            (weight_scale_inv), row-major: tile (i, j) at i * ceil(n/bs) + j.
- *   m, n     >= 1; need not be multiples of block_size.
+ *   m, n     >= 0 (either 0: nothing to do); need not be multiples of block_size.
  *   y        [m, n] out, dtype y_dtype: FP8BSQ_F32 gives fl32(DEC(x) * s);
  *            FP8BSQ_BF16 gives that product rounded to nearest even bf16.
  *
@@ -118,9 +123,9 @@ FP8BSQ_API int fp8_weight_dequant(const uint8_t *x, const float *s, int64_t m, i
  *
  *   x          [m, n] weights, dtype x_dtype (FP8BSQ_F32 or FP8BSQ_BF16),
  *              aligned to its element size.
- *   m, n       >= 1; need not be multiples of block_size (edge tiles use
- *              their valid elements only); m <= 65535 * 128 (else
- *              FP8BSQ_ERANGE).
+ *   m, n       >= 0 (either 0: nothing to do); need not be multiples of
+ *              block_size (edge tiles use their valid elements only);
+ *              m <= 65535 * 128 (else FP8BSQ_ERANGE).
  *   y          [m, n] E4M3 codes out.
  *   s          [ceil(m / block_size), ceil(n / block_size)] FP32 scales out,
  *              row-major, 4-byte aligned; fp8_weight_dequant(y, s) maps the
@@ -152,7 +157,8 @@ FP8BSQ_API int fp8_weight_quant(const void *x, int x_dtype, int64_t m, int64_t n
  *   b_s    [ceil(n / 128), k / 128] FP32 weight block scales.
  *   c      [m, n] out, dtype c_dtype (FP8BSQ_F32 or FP8BSQ_BF16, RNE from the
  *          FP32 accumulator); 4-byte aligned.
- *   m, n   >= 1; k >= 128 and k % 128 == 0 (else FP8BSQ_ESHAPE).
+ *   m, n   >= 0 (either 0: nothing to do); k >= 128 and k % 128 == 0 (else
+ *          FP8BSQ_ESHAPE; k = 0 is FP8BSQ_EINVAL).
  *
  * Accumulation order is not specified; every element is within
  * 1e-3 * sum_k |a_k * b_k| of the exact result (plus one bf16 ulp for BF16).
@@ -234,8 +240,8 @@ FP8BSQ_API int fp8_block_gemm_split(const uint8_t *a, const float *a_s, const ui
 /*
  * fp8_block_gemm_split_workspace -- bytes of workspace fp8_block_gemm_split
  * uses for an [m, k] x [n, k] product on the current HIP device: 0 when no
- * split pays for this shape there (the call then needs no workspace), or for
- * arguments fp8_block_gemm would reject.  Queries the device's compute-unit
+ * split pays for this shape there (the call then needs no workspace), for an
+ * empty product, or for arguments fp8_block_gemm would reject.  Queries the device's compute-unit
  * count; queues no work.
  */
 FP8BSQ_API size_t fp8_block_gemm_split_workspace(int64_t m, int64_t n, int64_t k);
@@ -289,7 +295,10 @@ FP8BSQ_API int fp8_block_gemm_split_noalloc(const uint8_t *a, const float *a_s, 
  *   bias       [n] of c's dtype, or NULL; added to the FP32 accumulator
  *              before the output rounding.
  *   c          [m, n] out, dtype c_dtype (FP8BSQ_F32 or FP8BSQ_BF16).
- *   m, n, k    m, n >= 1; k >= 128 and k % 128 == 0 (else FP8BSQ_ESHAPE).
+ *   m, n, k    m, n >= 0; k >= 128 and k % 128 == 0 (else FP8BSQ_ESHAPE; k = 0
+ *              is FP8BSQ_EINVAL).  m = 0: nothing to do.  n = 0: only a_q and
+ *              a_s are written (act_quant alone); b, b_s, bias and c are not
+ *              read and may be NULL.
  *   a_q        [m, k] E4M3 codes out (16-byte aligned): act_quant's y.
  *   a_s        [m, k / 128] FP32 scales out (4-byte aligned): act_quant's s.
  *

@@ -71,7 +71,7 @@ def test_act_quant_validation(lib):
     f = lib.fp8_act_quant
     assert f(None, 1, 8, 256, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 1, 8, 256, 128, 0, None, P, None) == _lib.EINVAL
-    assert f(P, 1, 0, 256, 128, 0, P, P, None) == _lib.EINVAL
+    assert f(P, 1, -1, 256, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 1, 8, -128, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 7, 8, 256, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 1, 8, 256, 128, 5, P, P, None) == _lib.EINVAL
@@ -85,7 +85,7 @@ def test_act_quant_validation(lib):
 def test_weight_dequant_validation(lib):
     f = lib.fp8_weight_dequant
     assert f(None, P, 8, 8, 128, P, 1, None) == _lib.EINVAL
-    assert f(P, P, 0, 8, 128, P, 1, None) == _lib.EINVAL
+    assert f(P, P, -1, 8, 128, P, 1, None) == _lib.EINVAL
     assert f(P, P, 8, 8, 128, P, 3, None) == _lib.EINVAL
     assert f(P, P, 8, 8, 256, P, 1, None) == _lib.EUNSUPPORTED
     assert f(P, P + 2, 8, 8, 128, P, 1, None) == _lib.EALIGN
@@ -97,7 +97,8 @@ def test_weight_dequant_validation(lib):
 def test_block_gemm_validation(lib, name):
     f = getattr(lib, name)
     assert f(None, P, P, P, P, 1, 16, 16, 128, None) == _lib.EINVAL
-    assert f(P, P, P, P, P, 1, 0, 16, 128, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, -1, 16, 128, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, 16, 16, 0, None) == _lib.EINVAL          # a product needs K
     assert f(P, P, P, P, P, 4, 16, 16, 128, None) == _lib.EINVAL
     assert f(P, P, P, P, P, 1, 16, 16, 100, None) == _lib.ESHAPE
     assert f(P + 8, P, P, P, P, 1, 16, 16, 128, None) == _lib.EALIGN
@@ -109,7 +110,7 @@ def test_block_gemm_validation(lib, name):
 def test_block_gemm_split_validation(lib):
     f = lib.fp8_block_gemm_split
     assert f(None, P, P, P, P, 1, 16, 16, 128, 0, P, 1024, None) == _lib.EINVAL
-    assert f(P, P, P, P, P, 1, 16, 0, 128, 0, P, 1024, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, 16, -1, 128, 0, P, 1024, None) == _lib.EINVAL
     assert f(P, P, P, P, P, 1, 16, 16, 128, 2, P, 1024, None) == _lib.EINVAL      # scale_fmt
     assert f(P, P, P, P, P, 1, 16, 16, 100, 0, P, 1024, None) == _lib.ESHAPE
     assert f(P, P, P, P, P, 1, 16, 16, 128, 0, P + 16, 1024, None) == _lib.EALIGN  # workspace
@@ -124,7 +125,7 @@ def test_block_gemm_split_validation(lib):
 def test_block_gemm_split_noalloc_validation(lib):
     f = lib.fp8_block_gemm_split_noalloc
     assert f(None, P, P, P, P, 1, 16, 16, 128, 0, None) == _lib.EINVAL
-    assert f(P, P, P, P, P, 1, 16, 0, 128, 0, None) == _lib.EINVAL
+    assert f(P, P, P, P, P, 1, 16, -1, 128, 0, None) == _lib.EINVAL
     assert f(P, P, P, P, P, 3, 16, 16, 128, 0, None) == _lib.EINVAL
     assert f(P, P, P, P, P, 1, 16, 16, 128, 2, None) == _lib.EINVAL      # scale_fmt
     assert f(P, P, P, P, P, 1, 16, 16, 100, 0, None) == _lib.ESHAPE
@@ -140,7 +141,7 @@ def test_weight_quant_validation(lib):
     assert f(None, 1, 8, 8, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 1, 8, 8, 128, 0, None, P, None) == _lib.EINVAL
     assert f(P, 1, 8, 8, 128, 0, P, None, None) == _lib.EINVAL
-    assert f(P, 1, 0, 8, 128, 0, P, P, None) == _lib.EINVAL
+    assert f(P, 1, -1, 8, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 1, 8, -1, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 2, 8, 8, 128, 0, P, P, None) == _lib.EINVAL
     assert f(P, 1, 8, 8, 128, 3, P, P, None) == _lib.EINVAL
@@ -166,7 +167,12 @@ def test_act_quant_gemm_validation(lib):
     assert call(a3=None) == _lib.EINVAL
     assert call(a11=None) == _lib.EINVAL
     assert call(a12=None) == _lib.EINVAL
-    assert call(a8=0) == _lib.EINVAL
+    assert call(a8=-1) == _lib.EINVAL
+    assert call(a10=0) == _lib.EINVAL                 # a product needs K
+    # no weight rows: the quantizer's pointers are still checked (a launch would follow)
+    assert call(a9=0, a0=None) == _lib.EINVAL
+    assert call(a9=0, a12=None) == _lib.EINVAL
+    assert call(a9=0, a11=P + 8) == _lib.EALIGN
     assert call(a1=5) == _lib.EINVAL
     assert call(a2=2) == _lib.EINVAL
     assert call(a7=9) == _lib.EINVAL
@@ -177,6 +183,40 @@ def test_act_quant_gemm_validation(lib):
     assert call(a12=P + 2) == _lib.EALIGN
     assert call(a5=P + 1) == _lib.EALIGN          # bf16 bias must be 2-byte aligned
     assert call(a8=1 << 40) == _lib.ERANGE
+
+
+def test_empty_inputs_return_ok_without_reading_pointers(lib):
+    """A call with no output elements returns FP8BSQ_OK before any pointer
+    check or HIP call (NULL pointers here; no GPU is needed), once the enum
+    and shape checks have passed."""
+    N = None
+    assert lib.fp8_act_quant(N, 1, 0, 256, 128, 0, N, N, N) == _lib.OK
+    assert lib.fp8_act_quant(N, 1, 8, 0, 128, 1, N, N, N) == _lib.OK
+    assert lib.fp8_act_quant(N, 1, 0, 200, 128, 0, N, N, N) == _lib.ESHAPE
+    assert lib.fp8_act_quant(N, 9, 0, 256, 128, 0, N, N, N) == _lib.EINVAL
+    assert lib.fp8_act_quant(N, 1, 0, 256, 64, 0, N, N, N) == _lib.EUNSUPPORTED
+    for f in (lib.fp8_weight_dequant,):
+        assert f(N, N, 0, 300, 128, N, 1, N) == _lib.OK
+        assert f(N, N, 300, 0, 128, N, 0, N) == _lib.OK
+        assert f(N, N, 0, 300, 128, N, 5, N) == _lib.EINVAL
+    assert lib.fp8_weight_quant(N, 1, 0, 300, 128, 1, N, N, N) == _lib.OK
+    assert lib.fp8_weight_quant(N, 0, 300, 0, 128, 0, N, N, N) == _lib.OK
+    assert lib.fp8_weight_quant(N, 0, 0, 300, 128, 4, N, N, N) == _lib.EINVAL
+    for name in ("fp8_block_gemm", "fp8_block_gemm_ue8m0", "fp8_block_gemm_reference"):
+        f = getattr(lib, name)
+        assert f(N, N, N, N, N, 1, 0, 256, 512, N) == _lib.OK, name
+        assert f(N, N, N, N, N, 0, 16, 0, 512, N) == _lib.OK, name
+        assert f(N, N, N, N, N, 1, 0, 256, 0, N) == _lib.EINVAL, name
+        assert f(N, N, N, N, N, 1, 0, 256, 100, N) == _lib.ESHAPE, name
+    assert lib.fp8_block_gemm_split(N, N, N, N, N, 1, 0, 256, 512, 1, N, 0, N) == _lib.OK
+    assert lib.fp8_block_gemm_split(N, N, N, N, N, 1, 16, 0, 512, 0, N, 0, N) == _lib.OK
+    assert lib.fp8_block_gemm_split(N, N, N, N, N, 1, 0, 256, 512, 3, N, 0, N) == _lib.EINVAL
+    assert lib.fp8_block_gemm_split_noalloc(N, N, N, N, N, 1, 0, 256, 512, 1, N) == _lib.OK
+    assert lib.fp8_block_gemm_split_noalloc(N, N, N, N, N, 0, 16, 0, 512, 0, N) == _lib.OK
+    assert lib.fp8_block_gemm_split_workspace(0, 256, 512) == 0
+    assert lib.fp8_act_quant_gemm(N, 1, 0, N, N, N, N, 1, 0, 256, 512, N, N, N) == _lib.OK
+    assert lib.fp8_act_quant_gemm(N, 1, 0, N, N, N, N, 1, 0, 0, 512, N, N, N) == _lib.OK
+    assert lib.fp8_act_quant_gemm(N, 1, 0, N, N, N, N, 1, 0, 256, 0, N, N, N) == _lib.EINVAL
 
 
 # ------------------------------------------------ dispatch (host-stub build only)
@@ -261,6 +301,18 @@ def test_dispatch_act_quant_gemm(lib):
     n2, name, ints, ptrs = st.last()
     assert n2 == n1 + 2 and name == "block_gemm"           # act_quant, then the GEMM
     assert ints[:5] == [0, 40, 256, 512, 0] and ptrs[:7] == [a_q, a_s, b, b_s, c, S, 0]
+    # no weight rows: act_quant alone, with b, b_s and c never read
+    assert lib.fp8_act_quant_gemm(x, 1, 1, None, None, None, None, 1, 40, 0, 512, a_q, a_s, S) == _lib.OK
+    n3, name, ints, ptrs = st.last()
+    assert n3 == n2 + 1 and name == "act_quant"
+    assert ints[:3] == [1, 160, 1] and ptrs[:4] == [x, a_q, a_s, S]
+    # empty calls launch nothing
+    for args in [(x, 1, 0, b, b_s, None, c, 1, 0, 256, 512, a_q, a_s, S)]:
+        assert lib.fp8_act_quant_gemm(*args) == _lib.OK
+    assert lib.fp8_block_gemm(None, None, None, None, None, 1, 0, 256, 512, S) == _lib.OK
+    assert lib.fp8_act_quant(None, 1, 0, 256, 128, 0, None, None, S) == _lib.OK
+    assert lib.fp8_weight_dequant(None, None, 0, 256, 128, None, 1, S) == _lib.OK
+    assert st.last()[0] == n3
 
 
 def test_launch_error_maps_to_elaunch(lib):
