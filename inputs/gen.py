@@ -92,6 +92,17 @@ def weight_codes(rng, n: int, k: int) -> np.ndarray:
     return c.astype(np.uint8)
 
 
+def weight_codes_chunks(seed: int, n: int, k: int, rows_per_chunk: int = 32768):
+    """The same distribution for matrices too large to build in one piece:
+    yields (first row, uint8 [rows, k]) in row order, from one generator
+    seeded with `seed`."""
+    rng = rng_for(seed)
+    for r0 in range(0, n, rows_per_chunk):
+        c = rng.integers(0, 254, size=(min(rows_per_chunk, n - r0), k), dtype=np.uint8)
+        c += c >= 0x7F                     # skip 0x7F; 254 -> 255 never drawn
+        yield r0, c
+
+
 def log_uniform_scales(rng, shape, lo: float, hi: float) -> np.ndarray:
     return (2.0 ** rng.uniform(lo, hi, size=shape)).astype(np.float32)
 
