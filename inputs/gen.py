@@ -85,6 +85,22 @@ def activations(rng, m: int, k: int, dtype: str = "bf16", outliers: bool = False
     raise ValueError(dtype)
 
 
+def activations_chunk(seed: int, m: int, k: int, index: int, rows_per_chunk: int = 16384):
+    """Chunk `index` (rows index * rows_per_chunk onward, as a bf16 CPU tensor) of
+    an [m, k] activation matrix too large to build in one piece, with the
+    prefill recipe (N(0,1), 0.1% outliers x100, one zero 1 x 128 block per
+    128-row group).  Each chunk draws from its own child stream of `seed`
+    (SeedSequence spawn key (index,)), so chunks can be built in any order or
+    in parallel.  Chunks hold whole 128-row groups."""
+    if rows_per_chunk % 128:
+        raise ValueError("rows_per_chunk must be a multiple of 128")
+    r0 = index * rows_per_chunk
+    if not 0 <= r0 < m:
+        raise ValueError("chunk index out of range")
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(index,)))
+    return activations(rng, min(rows_per_chunk, m - r0), k, outliers=True, zero_blocks=True)
+
+
 def weight_codes(rng, n: int, k: int) -> np.ndarray:
     """Uniform over the 254 finite E4M3 codes, uint8 [n, k]."""
     c = rng.integers(0, 254, size=(n, k), dtype=np.int16)
