@@ -208,14 +208,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 // 64 lanes x 16 bytes from base + voff (per lane) into LDS [lds, lds + 1024).
 __device__ __forceinline__ void lds_dma16(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
 // active lanes x 4 bytes from base + voff into LDS [lds + 4 * lane].
 __device__ __forceinline__ void lds_dma4(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
