@@ -280,17 +280,52 @@ class TimingEvents:
         self.events = []
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_gpu_for(ms, stream):
+    """Queue a spin kernel of about `ms` milliseconds on `stream` (torch's
+    _sleep), so that the host can queue the timed launches behind it: they then
+    run back to back, and no event interval holds host launch overhead."""
+    global _SLEEP_CYCLES_PER_MS
+    import torch
+    with torch.cuda.stream(stream):
+        if _SLEEP_CYCLES_PER_MS is None:
+            ev = TimingEvents(2)
+            torch.cuda._sleep(1000)
+            ev.record(0, stream)
+            torch.cuda._sleep(2_000_000)
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            _SLEEP_CYCLES_PER_MS = 2_000_000 / max(ev.elapsed_ms(0, 1), 1e-3)
+            ev.close()
+        torch.cuda._sleep(int(min(ms, 100.0) * _SLEEP_CYCLES_PER_MS))
+
+
 def time_launches(calls, reps, warmup, stream):
     """Mean and median microseconds of each call in `calls` (callables run in
-    order, once per repetition), from events recorded between them on `stream`."""
+    order, once per repetition), from events recorded between them on `stream`.
+    Where the warm-up shows the host queuing a repetition in more than a third
+    of the time the GPU takes to run it, the timed launches are queued behind a
+    spin kernel long enough for the host to queue them all, so that they run
+    back to back and no interval holds host launch overhead."""
     import numpy as np
     import torch
+    wev = TimingEvents(2)
+    wev.record(0, stream)
+    t0 = time.perf_counter()
     for _ in range(warmup):
         for c in calls:
             c()
+    host_ms = (time.perf_counter() - t0) * 1e3 / max(warmup, 1)
+    wev.record(1, stream)
     torch.cuda.synchronize()
+    gpu_ms = wev.elapsed_ms(0, 1) / max(warmup, 1)
+    wev.close()
     nc = len(calls)
     ev = TimingEvents((nc + 1) * reps)
+    if host_ms > gpu_ms / 3:
+        hold_gpu_for(2 * reps * host_ms + 1.0, stream)
     for r in range(reps):
         base = (nc + 1) * r
         ev.record(base, stream)
