@@ -686,8 +686,8 @@ struct DecodeSlot {
 // so the wider the workgroup the fewer fetches per weight row.  Five compute
 // waves give 231 workgroups for N = 18432, one per CU; three gave 384, two on
 // half the CUs, whose mover then sat ~1000 cycles per K block in DMA issue
-// (M = 64 with weights streaming from HBM: 50.7 us at three, 38.5 at five,
-// 40.7 at six).
+// (M = 64 with weights streaming from HBM, measured when this kernel still
+// served M = 64: 50.7 us at three, 38.5 at five, 40.7 at six).
 //
 // Activation scales (kTab): as in the tiled kernel, a double-buffered table of
 // kTabKb K blocks' scales per row, loaded one chunk ahead in 16-byte pieces;
