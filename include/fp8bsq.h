@@ -8,8 +8,11 @@
  * ---------------------------------------
  *  - Every data pointer is a DEVICE pointer (hipMalloc'd or a PyTorch CUDA
  *    tensor's data_ptr) owned by the caller, who keeps it alive until the work
- *    queued on `hip_stream` has finished.  The library allocates nothing and
- *    keeps no state between calls; calls are re-entrant and thread-safe.
+ *    queued on `hip_stream` has finished.  The library allocates nothing; its
+ *    only state is a per-device cache of the compute-unit count and the
+ *    static scratch of fp8_block_gemm_split_noalloc.  Calls are re-entrant
+ *    and thread-safe, except fp8_block_gemm_split_noalloc calls that overlap
+ *    on one GPU, which race on that scratch.
  *  - All tensors are dense and row-major.  E4M3 codes are bytes in the OCP
  *    E4M3FN encoding (PyTorch's torch.float8_e4m3fn).  Scales are FP32.
  *  - Work is queued on `hip_stream` (a hipStream_t; NULL = the default stream)
