@@ -620,8 +620,12 @@ constexpr int kDecodeMaxM = 64;
 constexpr int kDecodeMaxKb = 160;
 // Activations quantized inside the decode kernel (fused act_quant) for up to
 // this many rows: every workgroup quantizes all of them, so the redundant work
-// grows with m.
-constexpr int kFusedMaxM = 2;
+// grows with m.  The prologue runs on kFusedWaves waves, two per SIMD (the five
+// compute waves and three helpers that leave after it): measured against five
+// waves (one SIMD doing two waves' share) and against act_quant + GEMM as two
+// kernels, eight waves win up to four rows and lose from five.
+constexpr int kFusedMaxM = 4;
+constexpr int kFusedWaves = 8;
 
 // Fused prologue: quantize x [m, k] bf16 (m <= kFusedMaxM) per 1 x 128 block
 // exactly as the act_quant kernel does -- sixteen lanes per block, 8 elements
@@ -694,7 +698,7 @@ struct DecodeSlot {
 // otherwise each K block's kRows scales travel in its ring slot, one 4-byte
 // transfer per row.
 template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false>
-__global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_kernel(
+__global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 1)) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
@@ -801,11 +805,13 @@ __global__ __launch_bounds__(64 * (kDecodeCompute + 1)) void block_gemm_decode_k
   // for every load in flight).
   if constexpr (kFuseQ) {
     // `a` holds the bf16 activations; scale rows m..kRows-1 stay 0
-    for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kDecodeCompute) as_t[i / kRows][i % kRows] = 0.0f;
+    for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kFusedWaves) as_t[i / kRows][i % kRows] = 0.0f;
     __syncthreads();
-    fused_act_quant<kRows, 64 * kDecodeCompute>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q,
-                                                 a_s_out, blockIdx.x == 0);
+    fused_act_quant<kRows, 64 * kFusedWaves>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q,
+                                             a_s_out, blockIdx.x == 0);
     __syncthreads();
+    // the helper waves only quantize; the fused K loop has no barrier to miss
+    if (wave >= kDecodeCompute) return;
   }
   if (mover) {
     // the compute waves read block kb + 1 while they compute kb, so by the
@@ -1428,8 +1434,8 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
                                       const float *b_s, const void *bias, void *c, bool c_bf16,
                                       int64_t m, int64_t n, int64_t k, uint8_t *a_q, float *a_s,
                                       hipStream_t stream) {
-  // no mover: the compute waves only
-  const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * kDecodeCompute);
+  // no mover: the compute waves, and helpers for the prologue
+  const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * kFusedWaves);
   const size_t lds = (size_t)(m * k);
   if (c_bf16)
     hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecodeDepth, false, true>), grid, block, lds,

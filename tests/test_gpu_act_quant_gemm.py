@@ -1,6 +1,6 @@
 """GPU parity for fp8_act_quant_gemm (act_quant then the block GEMM, one call).
 
-For bf16 activations with m <= 2 the whole computation runs in one kernel
+For bf16 activations with m <= 4 the whole computation runs in one kernel
 (quantization in the GEMM's prologue); larger m and fp32 activations queue the
 two kernels.  Every case checks:
 
@@ -10,9 +10,10 @@ two kernels.  Every case checks:
   arithmetic;
 * C is within the oracle GEMM's bound (1e-3 * sum |a b|, + 1 bf16 ulp).
 
-Cases: the decode workloads M = 1, 2 (fused) and 3, 4, 8, 64 (two kernels), both
+Cases: the decode workloads M = 1-4 (fused) and 8, 64 (two kernels), both
 scale formats, fp32 output, ragged N, a single K block, the long-K decode
-shape (K = 18432), fp32 activations, and the Python binding.
+shape (K = 18432), the longest K the fused path takes (K / 128 = 160, its LDS
+at the most), fp32 activations, and the Python binding.
 """
 
 import numpy as np
@@ -57,10 +58,12 @@ def test_ue8m0_and_fp32_out(m):
     _run(d["x"], d["w"], d["w_s"], "ue8m0", "f32", "ue8m0/f32")
 
 
-# fused (bf16, m <= 2): one K block (k = 128) and three; a last batch of four
-# loads per lane that is only partly used (k = 18432: 288 blocks for 80 lanes x 4)
+# fused (bf16, m <= 4): one K block (k = 128) and three; a last batch of four
+# loads per lane that is only partly used (k = 18432, m = 2: 288 blocks for 32
+# sixteen-lane groups x 4); the longest K the fused path takes, at m = 4 (codes
+# of all of x in 80 KB of LDS); two kernels just above (m = 5, 7)
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 129, 128), (4, 17, 256), (2, 7168, 18432), (7, 500, 640),
-                                   (1, 129, 128), (2, 96, 384)])
+                                   (1, 129, 128), (2, 96, 384), (4, 300, 20480), (5, 200, 1024)])
 def test_shapes(m, n, k):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
     _run(d["x"], d["w"], d["w_s"], None, "bf16", "shape")
