@@ -620,12 +620,16 @@ constexpr int kDecodeMaxM = 64;
 constexpr int kDecodeMaxKb = 160;
 // Activations quantized inside the decode kernel (fused act_quant) for up to
 // this many rows: every workgroup quantizes all of them, so the redundant work
-// grows with m.  The prologue runs on kFusedWaves waves, two per SIMD (the five
-// compute waves and three helpers that leave after it): measured against five
-// waves (one SIMD doing two waves' share) and against act_quant + GEMM as two
-// kernels, eight waves win up to four rows and lose from five.
-constexpr int kFusedMaxM = 4;
-constexpr int kFusedWaves = 8;
+// grows with m.  The prologue runs on kFusedWaves waves, four per SIMD (the
+// five compute waves and eleven helpers that leave after it).  Measured
+// against act_quant + GEMM as two kernels, five waves (one SIMD doing two
+// waves' share) won up to two rows, eight waves up to four, sixteen up to five;
+// at six rows they break even.
+constexpr int kFusedMaxM = 5;
+constexpr int kFusedWaves = 16;
+// Most bytes of codes the fused prologue keeps in LDS (m * k), beside the five
+// weight rings and the scales: 80 KB keeps the workgroup within 160 KB.
+constexpr int64_t kFusedMaxCodes = 80 * 1024;
 
 // Fused prologue: quantize x [m, k] bf16 (m <= kFusedMaxM) per 1 x 128 block
 // exactly as the act_quant kernel does -- sixteen lanes per block, 8 elements
@@ -1447,7 +1451,7 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
 }
 
 bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k) {
-  return x_bf16 && m <= kFusedMaxM && k / kBlock <= kDecodeMaxKb;
+  return x_bf16 && m <= kFusedMaxM && k / kBlock <= kDecodeMaxKb && m * k <= kFusedMaxCodes;
 }
 
 }  // namespace fp8bsq

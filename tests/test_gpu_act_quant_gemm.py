@@ -1,6 +1,6 @@
 """GPU parity for fp8_act_quant_gemm (act_quant then the block GEMM, one call).
 
-For bf16 activations with m <= 4 the whole computation runs in one kernel
+For bf16 activations with m <= 5 (and m * k <= 80 K) the whole computation runs in one kernel
 (quantization in the GEMM's prologue); larger m and fp32 activations queue the
 two kernels.  Every case checks:
 
@@ -58,12 +58,14 @@ def test_ue8m0_and_fp32_out(m):
     _run(d["x"], d["w"], d["w_s"], "ue8m0", "f32", "ue8m0/f32")
 
 
-# fused (bf16, m <= 4): one K block (k = 128) and three; a last batch of four
-# loads per lane that is only partly used (k = 18432, m = 2: 288 blocks for 32
-# sixteen-lane groups x 4); the longest K the fused path takes, at m = 4 (codes
-# of all of x in 80 KB of LDS); two kernels just above (m = 5, 7)
+# fused (bf16, m <= 5, m * k <= 80 K): one K block (k = 128) and three; a last
+# batch of four loads per lane that is only partly used (k = 18432, m = 2: 288
+# blocks for 64 sixteen-lane groups x 4); the longest K the fused path takes, at
+# m = 4 (codes of all of x in 80 KB of LDS) and at m = 5; two kernels just past
+# those limits (m = 5 with one more K block, m = 6, 7)
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 129, 128), (4, 17, 256), (2, 7168, 18432), (7, 500, 640),
-                                   (1, 129, 128), (2, 96, 384), (4, 300, 20480), (5, 200, 1024)])
+                                   (1, 129, 128), (2, 96, 384), (4, 300, 20480), (5, 200, 1024),
+                                   (5, 200, 16384), (5, 200, 16512), (6, 130, 1024)])
 def test_shapes(m, n, k):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
     _run(d["x"], d["w"], d["w_s"], None, "bf16", "shape")
