@@ -24,7 +24,10 @@ Cache, so every kernel reads its inputs from HBM.
 on the same inputs in this process (the whole tensor where that takes seconds,
 a stated row sample for the prefill GEMMs).  Bandwidth-bound workloads cycle
 through enough copies of their buffers (at least 1 GB in all) that no launch
-finds its inputs in the Infinity Cache.
+finds its inputs in the Infinity Cache.  Each record gives the mean and the
+median of 50 timed launches; short kernels, whose Python launch overhead could
+otherwise leave the GPU waiting between them, are queued behind a spin kernel
+so that they run back to back.
 
 ``cpu_baseline`` times the CPU oracle (test infrastructure, never tuned) on a
 bounded sample of the step's workload: the first ``--cpu-rows`` activation rows
