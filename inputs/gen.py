@@ -16,6 +16,12 @@ the order activations, then weight codes, then weight scales):
   all-zero tile in every 8th row of tiles (tile column U[0, ceil(K/128)));
   then cast to bf16.
 
+Operands of 4 GiB and more (the size-limit tests) come in chunks:
+``weight_codes_chunks`` draws the weight-code distribution chunk by chunk from
+one generator, and ``activations_chunk`` builds one chunk of the activation
+recipe (outliers and zero blocks included) from its own child stream of the
+seed, so chunks can be built in parallel.
+
 Nothing here is part of the quantization method.
 """
 
