@@ -19,7 +19,7 @@ and, producing the GEMM's weight operand,
 * ``weight_quant(w, block_size=128, scale_fmt=None) -> (y, s)``
 
 and a linear layer's forward product in one call (act_quant, then fp8_gemm;
-a single kernel for bf16 decode batches of up to 5 rows),
+a single kernel for bf16 decode batches of up to 16 rows),
 
 * ``act_quant_gemm(x, b, b_s, scale_fmt=None, out_dtype=torch.bfloat16, bias=None) -> (c, y, s)``
 

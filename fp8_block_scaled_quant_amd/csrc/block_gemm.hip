@@ -607,57 +607,72 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 // prefetch ring; it was 20-45% slower at every M.)
 //
 // Fused act_quant (kFuseQ, M <= kFusedMaxM, bf16 activations): every
-// workgroup quantizes all of x [m, k] into LDS in its prologue with
-// act_quant's arithmetic (four blocks' loads in flight per lane), and
-// workgroup 0 also publishes the codes and scales; there is no mover and no
-// per-block barrier.  The compute waves do
-// the same arithmetic in the same order as on the two-call path, so both give
-// bit-identical outputs.
+// workgroup quantizes all of x [m, k] into LDS with act_quant's arithmetic,
+// and workgroup 0 also publishes the codes and scales; there is no mover and
+// no per-block barrier.  Eleven helper waves do the quantization while the
+// five compute waves already stream their weights: the helpers take x's
+// blocks in K order and count each finished block in LDS, and a compute wave
+// waits for a K block's count before it reads that block's codes.  The
+// compute waves do the same arithmetic in the same order as on the two-call
+// path, so both give bit-identical outputs.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeMaxM = 64;
 // Longest K (in K blocks) of the fused path, whose scales sit in LDS for the
 // whole run.
 constexpr int kDecodeMaxKb = 160;
 // Activations quantized inside the decode kernel (fused act_quant) for up to
-// this many rows: every workgroup quantizes all of them, so the redundant work
-// grows with m.  The prologue runs on kFusedWaves waves, four per SIMD (the
-// five compute waves and eleven helpers that leave after it).  Measured
-// against act_quant + GEMM as two kernels, five waves (one SIMD doing two
-// waves' share) won up to two rows, eight waves up to four, sixteen up to five;
-// at six rows they break even.
-constexpr int kFusedMaxM = 5;
+// this many rows (one 16-row MFMA tile), within the LDS limit below: every
+// workgroup quantizes all of them, but on helper waves that overlap the
+// weight stream, so the redundant work stays off the critical path.  The
+// workgroup has kFusedWaves waves, four per SIMD: five compute waves and
+// eleven helpers.
+constexpr int kFusedMaxM = 16;
 constexpr int kFusedWaves = 16;
-// Most bytes of codes the fused prologue keeps in LDS (m * k), beside the five
+constexpr int kFusedHelpers = kFusedWaves - 5;
+// Most bytes of codes the fused path keeps in LDS (m * k), beside the five
 // weight rings and the scales: 80 KB keeps the workgroup within 160 KB.
 constexpr int64_t kFusedMaxCodes = 80 * 1024;
 
-// Fused prologue: quantize x [m, k] bf16 (m <= kFusedMaxM) per 1 x 128 block
-// exactly as the act_quant kernel does -- sixteen lanes per block, 8 elements
-// each, amax over the 16-lane row, the same scale and quotient arithmetic --
-// into LDS codes aq [m][k] and scales as_t [kb][row].  Workgroup 0 also writes
-// the codes and scales to a_q / a_s_out, bit-identical to fp8_act_quant.
+// Fused act_quant on the helper waves (hq = thread index among them):
+// quantize x [m, k] bf16 per 1 x 128 block exactly as the act_quant kernel
+// does -- sixteen lanes per block, 8 elements each, amax over the 16-lane row,
+// the same scale and quotient arithmetic -- into LDS codes aq [m][k] and
+// scales as_t [kb][row].  Blocks go in K order (flat index kb * m + row, four
+// blocks' loads in flight per lane), so the K blocks the compute waves need
+// first are done first.  After a block's codes and scale are in LDS, its
+// first lane adds one to done[kb] and to done[kDecodeMaxKb] (all blocks) with
+// workgroup-scope release; a reader that sees done[kb] == m with acquire sees
+// the whole K block.  Workgroup 0 also writes the codes and scales to a_q /
+// a_s_out, bit-identical to fp8_act_quant.  The helpers start at a raised
+// wave priority for their first batch, whose blocks the compute waves wait
+// for first, and drop to the normal priority after it (measured: 2-4% faster
+// at M = 1-16 than either priority throughout).
 template <int kRows, int kThreadsQ, int kBatchQ = 4>
-__device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int m, int nkb,
-                                                bool ue8m0, uint8_t *aq, float (*as_t)[kRows],
-                                                uint8_t *__restrict__ a_q,
-                                                float *__restrict__ a_s_out, bool publish) {
-  const int t = threadIdx.x, row16 = t >> 4, sub = t & 15;
-  const int nblocks = m * nkb;                     // blocks of the flat [m * nkb, 128] sequence
+__device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int m, int nkb, int hq,
+                                                bool ue8m0, uint8_t *aq, float (*as_t)[kRows], int *done,
+                                                uint8_t *__restrict__ a_q, float *__restrict__ a_s_out,
+                                                bool publish) {
+  const int group = hq >> 4, sub = hq & 15;
+  const int nblocks = m * nkb;
   constexpr int kStride = kThreadsQ / 16;
-  // kBatchQ loads in flight per lane, then their blocks: one load latency per
-  // kBatchQ blocks instead of per block.  The sixteen lanes of a block share
-  // every condition below, as the row reduction needs.
-  for (int base = row16; base < nblocks; base += kBatchQ * kStride) {
+  // The sixteen lanes of a block share every condition below, as the row
+  // reduction needs.
+  for (int base = group; base < nblocks; base += kBatchQ * kStride) {
     u32x4 v[kBatchQ];
 #pragma unroll
     for (int u = 0; u < kBatchQ; ++u) {
-      const int blk = base + u * kStride;
-      if (blk < nblocks) v[u] = x[(int64_t)blk * 16 + sub];
+      const int idx = base + u * kStride;
+      if (idx < nblocks) {
+        const int kb = idx / m, row = idx - kb * m;
+        v[u] = x[((int64_t)row * nkb + kb) * 16 + sub];
+      }
     }
 #pragma unroll
     for (int u = 0; u < kBatchQ; ++u) {
-      const int blk = base + u * kStride;
-      if (blk >= nblocks) break;
+      const int idx = base + u * kStride;
+      if (idx >= nblocks) break;
+      const int kb = idx / m, row = idx - kb * m;
+      const int64_t blk = (int64_t)row * nkb + kb;
       u16x2 m2 = {0, 0};
       const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
@@ -667,14 +682,18 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
       float sc, r;
       block_scale_fast(amax, ue8m0, sc, r);
       const u32x2 codes = encode_chunk_bf16(v[u], sc, r);
-      *(u32x2 *)(aq + (int64_t)blk * kBlock + 8 * sub) = codes;
-      const int row = blk / nkb, kb = blk % nkb;
+      *(u32x2 *)(aq + blk * kBlock + 8 * sub) = codes;
       if (sub == 0) as_t[kb][row] = sc;
       if (publish) {
-        *(u32x2 *)(a_q + (int64_t)blk * kBlock + 8 * sub) = codes;
+        *(u32x2 *)(a_q + blk * kBlock + 8 * sub) = codes;
         if (sub == 0) a_s_out[blk] = sc;
       }
+      if (sub == 0) {
+        __hip_atomic_fetch_add(&done[kb], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&done[kDecodeMaxKb], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -707,7 +726,8 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
     float *__restrict__ a_s_out = nullptr) {
-  static_assert(!kFuseQ || kMT == 1, "the fused path covers m <= kFusedMaxM");
+  static_assert(!kFuseQ || (kMT == 1 && kFusedMaxM <= 16 && kDecodeCompute + kFusedHelpers == kFusedWaves),
+                "the fused path: one 16-row tile, five compute waves and the helpers");
   static_assert(kMT <= 2, "up to 32 activation rows");
   constexpr int kRows = 16 * kMT;
   constexpr int kLead = kDecodeLead;   // A blocks in flight ahead
@@ -719,6 +739,8 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
   // fused: codes [m][k] (dynamic) and scales [kb][row] of all of x
   extern __shared__ __attribute__((aligned(16))) uint8_t aq[];
   __shared__ float as_t[kFuseQ ? kDecodeMaxKb : 1][kRows];
+  // fused: blocks of x quantized, per K block and (last) in all
+  __shared__ int q_done[kFuseQ ? kDecodeMaxKb + 1 : 1];
   __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
   // weights: each compute wave DMAs its 16 weight rows into its own LDS ring
   // (whole-line transfers, half the vector-memory issue of fragment-shaped
@@ -810,12 +832,15 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
   if constexpr (kFuseQ) {
     // `a` holds the bf16 activations; scale rows m..kRows-1 stay 0
     for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kFusedWaves) as_t[i / kRows][i % kRows] = 0.0f;
-    __syncthreads();
-    fused_act_quant<kRows, 64 * kFusedWaves>((const u32x4 *)a, (int)m, nkb, ue8m0, aq, as_t, a_q,
-                                             a_s_out, blockIdx.x == 0);
+    for (int i = t; i <= kDecodeMaxKb; i += 64 * kFusedWaves) q_done[i] = 0;
     __syncthreads();
     // the helper waves only quantize; the fused K loop has no barrier to miss
-    if (wave >= kDecodeCompute) return;
+    if (wave >= kDecodeCompute) {
+      __builtin_amdgcn_s_setprio(3);
+      fused_act_quant<kRows, 64 * kFusedHelpers>((const u32x4 *)a, (int)m, nkb, t - 64 * kDecodeCompute,
+                                                 ue8m0, aq, as_t, q_done, a_q, a_s_out, blockIdx.x == 0);
+      return;
+    }
   }
   if (mover) {
     // the compute waves read block kb + 1 while they compute kb, so by the
@@ -847,10 +872,24 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
   f32x4 sa[2][kMT];
   float sb[2];
   const bool a_row_live = fr < m;   // fused: rows past m are zero fragments
+  int ready = 0;                     // fused: K blocks known to be quantized (wave-uniform)
   const uint8_t *a_lds = aq + (int64_t)(a_row_live ? fr : 0) * k + 16 * fq;
   auto read_a = [&](int kb, int buf) {   // kb may be nkb (a stale slot, never used)
     if constexpr (kFuseQ) {
       const int kbc = min(kb, nkb - 1);
+      if (kbc >= ready) {
+        // wait for the helpers to finish K block kbc (they wait on nothing,
+        // so this ends within microseconds; the bound only keeps a wave from
+        // spinning forever); once every block is done, stop checking
+        for (int spin = 0; spin < (1 << 20); ++spin) {
+          if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&q_done[kbc], __ATOMIC_ACQUIRE,
+                                                               __HIP_MEMORY_SCOPE_WORKGROUP)) >= m) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        ready = __builtin_amdgcn_readfirstlane(__hip_atomic_load(&q_done[kDecodeMaxKb], __ATOMIC_ACQUIRE,
+                                                                 __HIP_MEMORY_SCOPE_WORKGROUP)) >= m * nkb
+                    ? nkb : kbc + 1;
+      }
       af[buf][0] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (a_row_live) {
         const uint4 lo = *(const uint4 *)(a_lds + (int64_t)kbc * kBlock);
@@ -1438,7 +1477,7 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
                                       const float *b_s, const void *bias, void *c, bool c_bf16,
                                       int64_t m, int64_t n, int64_t k, uint8_t *a_q, float *a_s,
                                       hipStream_t stream) {
-  // no mover: the compute waves, and helpers for the prologue
+  // no mover: the compute waves, and the helpers that quantize x
   const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * kFusedWaves);
   const size_t lds = (size_t)(m * k);
   if (c_bf16)

@@ -116,8 +116,10 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
   return result();
 }
 
-// the stand-in fuses bf16 activations of up to 5 rows
-bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k) { return x_bf16 && m <= 5 && k > 0; }
+// the stand-in fuses bf16 activations of up to 16 rows and 80 K codes
+bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k) {
+  return x_bf16 && m <= 16 && k > 0 && m * k <= 81920;
+}
 
 }  // namespace fp8bsq
 
