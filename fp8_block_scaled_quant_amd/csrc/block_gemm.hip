@@ -621,17 +621,30 @@ constexpr int kDecodeMaxM = 64;
 // whole run.
 constexpr int kDecodeMaxKb = 160;
 // Activations quantized inside the decode kernel (fused act_quant) for up to
-// this many rows (one 16-row MFMA tile), within the LDS limit below: every
+// this many rows (one 16-row MFMA tile), within the code limits below: every
 // workgroup quantizes all of them, but on helper waves that overlap the
 // weight stream, so the redundant work stays off the critical path.  The
 // workgroup has kFusedWaves waves, four per SIMD: five compute waves and
 // eleven helpers.
 constexpr int kFusedMaxM = 16;
 constexpr int kFusedWaves = 16;
-constexpr int kFusedHelpers = kFusedWaves - 5;
-// Most bytes of codes the fused path keeps in LDS (m * k), beside the five
-// weight rings and the scales: 80 KB keeps the workgroup within 160 KB.
+constexpr int kFusedCompute = 5;
+constexpr int kFusedHelpers = kFusedWaves - kFusedCompute;
+// Most bytes of codes the fused path keeps in LDS, beside the five weight
+// rings and the scales: 80 KB keeps the workgroup within 160 KB.  Up to that
+// many codes (m * k) all of x stays in LDS; beyond it, up to
+// kFusedRingMaxCodes, the codes go through a ring of fused_ring_blocks(m) K
+// blocks that the helpers refill as the compute waves finish reading them.
+// Past that limit the redundant quantization outweighs the saved kernel
+// boundary (measured at N = 7168, K = 18432: 8% slower at m = 12, 18% at 16).
 constexpr int64_t kFusedMaxCodes = 80 * 1024;
+constexpr int64_t kFusedRingMaxCodes = 120 * 1024;
+// K blocks of m rows' codes in the ring: the largest power of two that fits.
+__host__ __device__ constexpr int fused_ring_blocks(int m) {
+  int r = 1;
+  while (2 * r * m * kBlock <= kFusedMaxCodes) r *= 2;
+  return r;
+}
 
 // Fused act_quant on the helper waves (hq = thread index among them):
 // quantize x [m, k] bf16 per 1 x 128 block exactly as the act_quant kernel
@@ -642,17 +655,21 @@ constexpr int64_t kFusedMaxCodes = 80 * 1024;
 // first are done first.  After a block's codes and scale are in LDS, its
 // first lane adds one to done[kb] and to done[kDecodeMaxKb] (all blocks) with
 // workgroup-scope release; a reader that sees done[kb] == m with acquire sees
-// the whole K block.  Workgroup 0 also writes the codes and scales to a_q /
+// the whole K block.  With kRing, block kb's codes go to ring slot
+// kb & ring_mask, and a helper first waits until every compute wave has
+// finished reading the slot's previous block (prog[w]: K blocks wave w has
+// read).  Workgroup 0 also writes the codes and scales to a_q /
 // a_s_out, bit-identical to fp8_act_quant.  The helpers start at a raised
 // wave priority for their first batch, whose blocks the compute waves wait
 // for first, and drop to the normal priority after it (measured: 2-4% faster
 // at M = 1-16 than either priority throughout).
-template <int kRows, int kThreadsQ, int kBatchQ = 4>
+template <int kRows, int kThreadsQ, bool kRing, int kBatchQ = 4>
 __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int m, int nkb, int hq,
                                                 bool ue8m0, uint8_t *aq, float (*as_t)[kRows], int *done,
-                                                uint8_t *__restrict__ a_q, float *__restrict__ a_s_out,
-                                                bool publish) {
+                                                const int *prog, int ring_mask, uint8_t *__restrict__ a_q,
+                                                float *__restrict__ a_s_out, bool publish) {
   const int group = hq >> 4, sub = hq & 15;
+  int seen = 0;   // K blocks every compute wave has read, as last looked up
   const int nblocks = m * nkb;
   constexpr int kStride = kThreadsQ / 16;
   // The sixteen lanes of a block share every condition below, as the row
@@ -682,7 +699,24 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
       float sc, r;
       block_scale_fast(amax, ue8m0, sc, r);
       const u32x2 codes = encode_chunk_bf16(v[u], sc, r);
-      *(u32x2 *)(aq + blk * kBlock + 8 * sub) = codes;
+      if constexpr (kRing) {
+        // the compute waves only wait on the helpers' older blocks, so this
+        // ends; the bound only keeps a wave from spinning forever
+        if (kb > seen + ring_mask) {
+          for (int spin = 0; spin < (1 << 20); ++spin) {
+            int lo = __hip_atomic_load(&prog[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+            for (int w = 1; w < kFusedCompute; ++w)
+              lo = min(lo, __hip_atomic_load(&prog[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+            seen = lo;
+            if (kb <= seen + ring_mask) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+        *(u32x2 *)(aq + ((int64_t)(kb & ring_mask) * m + row) * kBlock + 8 * sub) = codes;
+      } else {
+        *(u32x2 *)(aq + blk * kBlock + 8 * sub) = codes;
+      }
       if (sub == 0) as_t[kb][row] = sc;
       if (publish) {
         *(u32x2 *)(a_q + blk * kBlock + 8 * sub) = codes;
@@ -720,14 +754,15 @@ struct DecodeSlot {
 // kTabKb K blocks' scales per row, loaded one chunk ahead in 16-byte pieces;
 // otherwise each K block's kRows scales travel in its ring slot, one 4-byte
 // transfer per row.
-template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false>
+template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false, bool kRing = false>
 __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 1)) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
     float *__restrict__ a_s_out = nullptr) {
-  static_assert(!kFuseQ || (kMT == 1 && kFusedMaxM <= 16 && kDecodeCompute + kFusedHelpers == kFusedWaves),
+  static_assert(!kFuseQ || (kMT == 1 && kFusedMaxM <= 16 && kDecodeCompute == kFusedCompute),
                 "the fused path: one 16-row tile, five compute waves and the helpers");
+  static_assert(!kRing || kFuseQ, "the ring belongs to the fused path");
   static_assert(kMT <= 2, "up to 32 activation rows");
   constexpr int kRows = 16 * kMT;
   constexpr int kLead = kDecodeLead;   // A blocks in flight ahead
@@ -736,11 +771,14 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
   // table: [32-row block][half][row][4 K blocks], as the DMA lanes lay it down
   constexpr int kTabRows = (kRows + 31) / 32 * 32;   // whole 32-row blocks (one DMA each)
   __shared__ __attribute__((aligned(1024))) DecodeSlot<kMT> ring[kFuseQ ? 1 : kSlots];
-  // fused: codes [m][k] (dynamic) and scales [kb][row] of all of x
+  // fused: codes [m][k] (dynamic; with kRing [slot][m][128]) and scales
+  // [kb][row] of all of x
   extern __shared__ __attribute__((aligned(16))) uint8_t aq[];
   __shared__ float as_t[kFuseQ ? kDecodeMaxKb : 1][kRows];
   // fused: blocks of x quantized, per K block and (last) in all
   __shared__ int q_done[kFuseQ ? kDecodeMaxKb + 1 : 1];
+  // fused with the ring: K blocks each compute wave has finished reading
+  __shared__ int q_prog[kRing ? kDecodeCompute : 1];
   __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
   // weights: each compute wave DMAs its 16 weight rows into its own LDS ring
   // (whole-line transfers, half the vector-memory issue of fragment-shaped
@@ -829,16 +867,19 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
   // branch-free: the compiler's count of weight loads in flight stays exact,
   // and no ring register is merged across paths (either would make it wait
   // for every load in flight).
+  const int ring_mask = kRing ? fused_ring_blocks((int)m) - 1 : 0;
   if constexpr (kFuseQ) {
     // `a` holds the bf16 activations; scale rows m..kRows-1 stay 0
     for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kFusedWaves) as_t[i / kRows][i % kRows] = 0.0f;
     for (int i = t; i <= kDecodeMaxKb; i += 64 * kFusedWaves) q_done[i] = 0;
+    if (kRing && t < kDecodeCompute) q_prog[t] = 0;
     __syncthreads();
     // the helper waves only quantize; the fused K loop has no barrier to miss
     if (wave >= kDecodeCompute) {
       __builtin_amdgcn_s_setprio(3);
-      fused_act_quant<kRows, 64 * kFusedHelpers>((const u32x4 *)a, (int)m, nkb, t - 64 * kDecodeCompute,
-                                                 ue8m0, aq, as_t, q_done, a_q, a_s_out, blockIdx.x == 0);
+      fused_act_quant<kRows, 64 * kFusedHelpers, kRing>((const u32x4 *)a, (int)m, nkb, t - 64 * kDecodeCompute,
+                                                        ue8m0, aq, as_t, q_done, q_prog, ring_mask, a_q, a_s_out,
+                                                        blockIdx.x == 0);
       return;
     }
   }
@@ -873,7 +914,7 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
   float sb[2];
   const bool a_row_live = fr < m;   // fused: rows past m are zero fragments
   int ready = 0;                     // fused: K blocks known to be quantized (wave-uniform)
-  const uint8_t *a_lds = aq + (int64_t)(a_row_live ? fr : 0) * k + 16 * fq;
+  const uint8_t *a_lds = aq + (int64_t)(a_row_live ? fr : 0) * (kRing ? kBlock : k) + 16 * fq;
   auto read_a = [&](int kb, int buf) {   // kb may be nkb (a stale slot, never used)
     if constexpr (kFuseQ) {
       const int kbc = min(kb, nkb - 1);
@@ -892,8 +933,9 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
       }
       af[buf][0] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (a_row_live) {
-        const uint4 lo = *(const uint4 *)(a_lds + (int64_t)kbc * kBlock);
-        const uint4 hi = *(const uint4 *)(a_lds + (int64_t)kbc * kBlock + 64);
+        const uint8_t *codes = kRing ? a_lds + (kbc & ring_mask) * (int)m * kBlock : a_lds + (int64_t)kbc * kBlock;
+        const uint4 lo = *(const uint4 *)codes;
+        const uint4 hi = *(const uint4 *)(codes + 64);
         af[buf][0] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
       sa[buf][0] = *(const f32x4 *)&as_t[kbc][4 * fq];
@@ -948,6 +990,9 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
     compute(bf[cur], cur);
     issue_b(min(kb + kDepth, nkb - 1));
     if (!kFuseQ) workgroup_barrier();   // hands the mover's A ring on
+    // fused, ring: blocks 0..kb are read (block kb's codes fed this step's
+    // MFMA; the release orders those reads before the helpers' refill)
+    if (kRing) __hip_atomic_store(&q_prog[wave], kb + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue_b(min(d, nkb - 1));
@@ -1479,18 +1524,26 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
                                       hipStream_t stream) {
   // no mover: the compute waves, and the helpers that quantize x
   const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * kFusedWaves);
-  const size_t lds = (size_t)(m * k);
-  if (c_bf16)
-    hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecodeDepth, false, true>), grid, block, lds,
-                       stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
+  // all of x's codes in LDS, or (more of them) a ring of K blocks
+#define FP8BSQ_FUSED(RING, LDS)                                                                               \
+  do {                                                                                                         \
+    if (c_bf16)                                                                                                \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecodeDepth, false, true, RING>), grid, block,     \
+                         (LDS), stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s); \
+    else                                                                                                       \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecodeDepth, false, true, RING>), grid, block,    \
+                         (LDS), stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s); \
+  } while (0)
+  if (m * k <= kFusedMaxCodes)
+    FP8BSQ_FUSED(false, (size_t)(m * k));
   else
-    hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecodeDepth, false, true>), grid, block, lds,
-                       stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s);
+    FP8BSQ_FUSED(true, (size_t)fused_ring_blocks((int)m) * m * kBlock);
+#undef FP8BSQ_FUSED
   return hipGetLastError();
 }
 
 bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k) {
-  return x_bf16 && m <= kFusedMaxM && k / kBlock <= kDecodeMaxKb && m * k <= kFusedMaxCodes;
+  return x_bf16 && m <= kFusedMaxM && k / kBlock <= kDecodeMaxKb && m * k <= kFusedRingMaxCodes;
 }
 
 }  // namespace fp8bsq

@@ -6,7 +6,8 @@ in one 1 x 128 block may change that block's codes and scale only: every other
 block must still match the oracle bit for bit, and the canary bands around
 every output must be untouched.  Checked for bf16 and fp32 activations, both
 scale formats, and for the one-kernel act_quant_gemm path (m <= 16), whose
-helper waves quantize x in every workgroup.
+helper waves quantize x in every workgroup (with all of x in LDS, and through
+the LDS ring at m = 16, k = 7168).
 """
 
 import numpy as np
@@ -64,15 +65,15 @@ def test_act_quant_confines_non_finite_blocks(dtype, fmt):
     assert np.array_equal(codes[cb], wq[cb])
 
 
-@pytest.mark.parametrize("m", [1, 5, 16])
-def test_fused_act_quant_gemm_confines_non_finite_blocks(m):
-    d = gen.custom_gemm(seed=93 + m, m=m, n=700, k=2048)
+@pytest.mark.parametrize("m,k", [(1, 2048), (5, 2048), (16, 2048), (16, 7168)])
+def test_fused_act_quant_gemm_confines_non_finite_blocks(m, k):
+    d = gen.custom_gemm(seed=93 + m, m=m, n=700, k=k)
     x = d["x"]
     hit = _plant(x, 94 + m, 3)
-    G.announce(f"act_quant_gemm m={m} with {len(hit)} non-finite blocks")
+    G.announce(f"act_quant_gemm m={m} k={k} with {len(hit)} non-finite blocks")
     _, codes, scales = G.act_quant_gemm(x.to(G.device()), d["w"], d["w_s"], None, "bf16")
     wq, ws = _expect(x, None)
-    clean = _clean_mask(m, 2048, hit)
+    clean = _clean_mask(m, k, hit)
     assert np.array_equal(scales.view(np.uint32)[clean], ws.view(np.uint32)[clean])
     cb = np.repeat(clean, 128, axis=1)
     assert np.array_equal(codes[cb], wq[cb])
