@@ -731,8 +731,8 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
   }
 }
 
-constexpr int kDecodeCompute = 5;                // compute waves per workgroup (plus the mover)
-constexpr int kDecodeRows = 16 * kDecodeCompute;   // weight rows per workgroup
+constexpr int kDecodeCompute = 5;                // most compute waves per workgroup (plus the mover)
+constexpr int kDecodeRows = 16 * kDecodeCompute;   // weight rows per workgroup at that width
 constexpr int kDecodeLead = 6;                   // K blocks of A in flight ahead of use (ring: one more slot)
 constexpr int kDecodeDepth = 6;                  // weight ring depth per compute wave
 
@@ -742,25 +742,32 @@ struct DecodeSlot {
   float s[16 * kMT];              // a_s of the K block, per row
 };
 
-// Workgroup size: each workgroup fetches its K blocks of A and their scales
-// once, and the CU's vector-memory issue rate (not HBM) bounded the kernel,
-// so the wider the workgroup the fewer fetches per weight row.  Five compute
-// waves give 231 workgroups for N = 18432, one per CU; three gave 384, two on
-// half the CUs, whose mover then sat ~1000 cycles per K block in DMA issue
-// (M = 64 with weights streaming from HBM, measured when this kernel still
-// served M = 64: 50.7 us at three, 38.5 at five, 40.7 at six).
+// Workgroup size (kCW compute waves): each workgroup fetches its K blocks of
+// A and their scales once, and the CU's vector-memory issue rate (not HBM)
+// bounded the kernel, so the wider the workgroup the fewer fetches per weight
+// row.  Five compute waves give 231 workgroups for N = 18432, one per CU;
+// three gave 384, two on half the CUs, whose mover then sat ~1000 cycles per
+// K block in DMA issue (M = 64 with weights streaming from HBM, measured when
+// this kernel still served M = 64: 50.7 us at three, 38.5 at five, 40.7 at
+// six).  A narrower weight leaves CUs idle at five waves (N = 7168: 90
+// workgroups), so the launch takes the fewest waves that keep the grid within
+// one workgroup per CU: two at N = 7168 (224 workgroups) measured 19-21%
+// faster than five at M = 1-32, and 8-10% faster than one (448) or three
+// (150), bit-identical.
 //
 // Activation scales (kTab): as in the tiled kernel, a double-buffered table of
 // kTabKb K blocks' scales per row, loaded one chunk ahead in 16-byte pieces;
 // otherwise each K block's kRows scales travel in its ring slot, one 4-byte
 // transfer per row.
-template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false, bool kRing = false>
-__global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 1)) void block_gemm_decode_kernel(
+template <bool kBf16Out, int kMT, int kDepth, bool kTab, bool kFuseQ = false, bool kRing = false,
+          int kCW = kDecodeCompute>
+__global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kCW + 1)) void block_gemm_decode_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
     float *__restrict__ a_s_out = nullptr) {
-  static_assert(!kFuseQ || (kMT == 1 && kFusedMaxM <= 16 && kDecodeCompute == kFusedCompute),
+  static_assert(kCW >= 1 && kCW <= kDecodeCompute, "one to five compute waves");
+  static_assert(!kFuseQ || (kMT == 1 && kFusedMaxM <= 16 && kCW == kFusedCompute),
                 "the fused path: one 16-row tile, five compute waves and the helpers");
   static_assert(!kRing || kFuseQ, "the ring belongs to the fused path");
   static_assert(kMT <= 2, "up to 32 activation rows");
@@ -778,15 +785,15 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
   // fused: blocks of x quantized, per K block and (last) in all
   __shared__ int q_done[kFuseQ ? kDecodeMaxKb + 1 : 1];
   // fused with the ring: K blocks each compute wave has finished reading
-  __shared__ int q_prog[kRing ? kDecodeCompute : 1];
+  __shared__ int q_prog[kRing ? kCW : 1];
   __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
   // weights: each compute wave DMAs its 16 weight rows into its own LDS ring
   // (whole-line transfers, half the vector-memory issue of fragment-shaped
   // loads)
-  __shared__ __attribute__((aligned(1024))) uint8_t bring[kDecodeCompute][kDepth][16 * kBlock];
+  __shared__ __attribute__((aligned(1024))) uint8_t bring[kCW][kDepth][16 * kBlock];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool mover = !kFuseQ && wave == kDecodeCompute;
+  const bool mover = !kFuseQ && wave == kCW;
   const int nkb = (int)(k / kBlock);
 
   // mover: lane p of row group g fills chunk slot p % 8 of row 8 g + p / 8;
@@ -837,7 +844,7 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
     }
   };
 
-  const int64_t n0 = (int64_t)blockIdx.x * kDecodeRows + 16 * (mover ? 0 : wave);
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * kCW) + 16 * (mover ? 0 : wave);
   const int fr = lane & 15, fq = lane >> 4;
   const float *bs_row = b_s + min(n0 / kBlock, (n - 1) / kBlock) * nkb;
   // Each compute wave DMAs its own 16 weight rows of a K block (two
@@ -872,12 +879,12 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kDecodeCompute + 
     // `a` holds the bf16 activations; scale rows m..kRows-1 stay 0
     for (int i = t; i < kDecodeMaxKb * kRows; i += 64 * kFusedWaves) as_t[i / kRows][i % kRows] = 0.0f;
     for (int i = t; i <= kDecodeMaxKb; i += 64 * kFusedWaves) q_done[i] = 0;
-    if (kRing && t < kDecodeCompute) q_prog[t] = 0;
+    if (kRing && t < kCW) q_prog[t] = 0;
     __syncthreads();
     // the helper waves only quantize; the fused K loop has no barrier to miss
-    if (wave >= kDecodeCompute) {
+    if (wave >= kCW) {
       __builtin_amdgcn_s_setprio(3);
-      fused_act_quant<kRows, 64 * kFusedHelpers, kRing>((const u32x4 *)a, (int)m, nkb, t - 64 * kDecodeCompute,
+      fused_act_quant<kRows, 64 * kFusedHelpers, kRing>((const u32x4 *)a, (int)m, nkb, t - 64 * kCW,
                                                         ue8m0, aq, as_t, q_done, q_prog, ring_mask, a_q, a_s_out,
                                                         blockIdx.x == 0);
       return;
@@ -1460,17 +1467,33 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && kWideRows * k < ((int64_t)1 << 32)) {
     const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
+    // the decode kernel's compute waves per workgroup: the fewest that keep
+    // its grid within one workgroup per CU (five if the CU count is unknown)
+    const int64_t cus = current_device_cus();
+    const int64_t want = cus > 0 ? (n + 16 * cus - 1) / (16 * cus) : kDecodeCompute;
+    const int cw = want < 1 ? 1 : want > kDecodeCompute ? kDecodeCompute : (int)want;
+    const dim3 dgrid((unsigned)((n + 16 * cw - 1) / (16 * cw)));
     // up to 32 rows: the decode kernel with MT activation row tiles per
     // compute wave; above: the wide kernel with AT row tiles, one per wave
+#define FP8BSQ_DECODE_W(MT, TAB, CW)                                                                        \
+  do {                                                                                                       \
+    const dim3 block(64 * ((CW) + 1));                                                                       \
+    if (c_bf16)                                                                                              \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, kDecodeDepth, TAB, false, false, CW>), dgrid,   \
+                         block, 0, stream, a, a_s, b, b_s, c, m, n, k, bias);                                \
+    else                                                                                                     \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, kDecodeDepth, TAB, false, false, CW>), dgrid,  \
+                         block, 0, stream, a, a_s, b, b_s, c, m, n, k, bias);                                \
+  } while (0)
 #define FP8BSQ_DECODE_T(MT, TAB)                                                                            \
   do {                                                                                                       \
-    const dim3 block(64 * (kDecodeCompute + 1));                                                             \
-    if (c_bf16)                                                                                              \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<true, MT, kDecodeDepth, TAB>), grid, block, 0, stream, a, \
-                         a_s, b, b_s, c, m, n, k, bias);                                                     \
-    else                                                                                                     \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<false, MT, kDecodeDepth, TAB>), grid, block, 0, stream,   \
-                         a, a_s, b, b_s, c, m, n, k, bias);                                                  \
+    switch (cw) {                                                                                            \
+      case 1: FP8BSQ_DECODE_W(MT, TAB, 1); break;                                                            \
+      case 2: FP8BSQ_DECODE_W(MT, TAB, 2); break;                                                            \
+      case 3: FP8BSQ_DECODE_W(MT, TAB, 3); break;                                                            \
+      case 4: FP8BSQ_DECODE_W(MT, TAB, 4); break;                                                            \
+      default: FP8BSQ_DECODE_W(MT, TAB, kDecodeCompute); break;                                              \
+    }                                                                                                        \
   } while (0)
 #define FP8BSQ_DECODE(MT)                                                                                   \
   do {                                                                                                       \
@@ -1500,6 +1523,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
 #undef FP8BSQ_WIDE_T
 #undef FP8BSQ_DECODE
 #undef FP8BSQ_DECODE_T
+#undef FP8BSQ_DECODE_W
     return hipGetLastError();
   }
   return launch_block_gemm_reference(a, a_s, b, b_s, c, c_bf16, m, n, k, stream, bias);
