@@ -1028,55 +1028,59 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kCW + 1)) void bl
 
 // ---------------------------------------------------------------------------
 // Wide decode kernel for 32 < M <= 64: the weight tiles are shared, the
-// activation tiles are not.  A workgroup owns 80 weight rows (five 16-row
-// tiles) and all of A's row tiles (kAT = 3 or 4); compute wave w owns A's row
-// tile w and runs it against all five weight tiles, so each K block a wave
-// reads one A fragment and five weight fragments, and the MFMA and rescale
-// work sits evenly on the four SIMDs.  Two mover waves fill a kWideSlots-slot
-// LDS ring kWideLead blocks ahead: one DMAs each K block's A rows and (without
-// the table) their scales, the other its 80 weight rows.  Each waits on its
+// activation tiles are not.  A workgroup owns kWT 16-row weight tiles (up to
+// five, 80 rows) and all of A's row tiles (kAT = 3 or 4); compute wave w owns
+// A's row tile w and runs it against all kWT weight tiles, so each K block a
+// wave reads one A fragment and kWT weight fragments, and the MFMA and
+// rescale work sits evenly on the four SIMDs.  Two mover waves fill a
+// kWideSlots-slot LDS ring kWideLead blocks ahead: one DMAs each K block's A
+// rows and (without the table) their scales, the other its weight rows.  Each waits on its
 // own transfers only, and one barrier per K block hands the ring on, as in the
 // decode kernel.  (One mover for both measured 1-3% slower.)  Against two
 // compute waves per weight tile, each DMAing its own copy of the tile's rows,
 // this measured 7-11% faster at M = 33-64 with bit-identical outputs (each
 // output element sees the same FMAs in the same order); at M <= 32 it
-// measured no faster than the decode kernel, and at M <= 16 2% slower.
+// measured no faster than the decode kernel, and at M <= 16 2% slower.  As
+// for the decode kernel, the launch takes the fewest weight tiles that keep
+// the grid within one workgroup per CU: at N = 4096 and 7168 (one and two
+// tiles) 24-27% faster than five tiles, at 12288 (three) 16%.
 // ---------------------------------------------------------------------------
-constexpr int kWideTiles = 5;                    // weight tiles per workgroup
-constexpr int kWideRows = 16 * kWideTiles;       // weight rows per workgroup (as kDecodeRows)
+constexpr int kWideTiles = 5;                    // most weight tiles per workgroup
+constexpr int kWideRows = 16 * kWideTiles;       // weight rows per workgroup at that width
 constexpr int kWideLead = 5;                     // K blocks in flight ahead of use
 constexpr int kWideSlots = kWideLead + 1;
 
-template <int kAT>
+template <int kAT, int kWT>
 struct WideSlot {
   uint8_t a[16 * kAT * kBlock];    // [row][16-byte chunk slot], swizzled
-  uint8_t b[kWideRows * kBlock];   // the same for the weight rows
+  uint8_t b[16 * kWT * kBlock];    // the same for the weight rows
   float s[16 * kAT];               // a_s of the K block, per row (no table)
 };
 
-template <bool kBf16Out, int kAT, bool kTab>
+template <bool kBf16Out, int kAT, bool kTab, int kWT = kWideTiles>
 __global__ __launch_bounds__(64 * (kAT + 2)) void block_gemm_decode_wide_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_s, const uint8_t *__restrict__ b,
     const float *__restrict__ b_s, void *__restrict__ c, int64_t m, int64_t n, int64_t k,
     const void *__restrict__ bias) {
   constexpr int kRows = 16 * kAT;
+  constexpr int kWRows = 16 * kWT;
   // transfers per K block of the A mover and of the weight mover
-  constexpr int kDmaA = kRows / 8 + (kTab ? 0 : 1), kDmaB = kWideRows / 8;
+  constexpr int kDmaA = kRows / 8 + (kTab ? 0 : 1), kDmaB = kWRows / 8;
   static_assert((kWideLead - 2) * kDmaB < 64 && (kWideLead - 2) * kDmaA < 64, "the wait counter's range");
   constexpr int kTabRows = (kRows + 31) / 32 * 32;
-  __shared__ __attribute__((aligned(1024))) WideSlot<kAT> ring[kWideSlots];
+  __shared__ __attribute__((aligned(1024))) WideSlot<kAT, kWT> ring[kWideSlots];
   __shared__ __attribute__((aligned(16))) float stab[kTab ? 2 : 1][kTab ? kTabRows * kTabKb : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool mover = wave >= kAT, bmover = wave == kAT + 1;
   const int nkb = (int)(k / kBlock);
-  const int64_t n0 = (int64_t)blockIdx.x * kWideRows;
+  const int64_t n0 = (int64_t)blockIdx.x * kWRows;
 
   if (mover) {
     // lane p of row group g fills chunk slot p % 8 of row 8 g + p / 8; A rows
     // past m re-read row m - 1, weight rows past n row n - 1
     const int dr = lane >> 3, ds = lane & 7;
-    uint32_t a_off[kRows / 8], b_off[kWideRows / 8];
+    uint32_t a_off[kRows / 8], b_off[kWRows / 8];
 #pragma unroll
     for (int g = 0; g < kRows / 8; ++g) {
       const int row = 8 * g + dr;
@@ -1085,21 +1089,21 @@ __global__ __launch_bounds__(64 * (kAT + 2)) void block_gemm_decode_wide_kernel(
     const int64_t nb0 = min(n0, n - 1);
     const uint8_t *b_base = b + nb0 * k;
 #pragma unroll
-    for (int g = 0; g < kWideRows / 8; ++g) {
+    for (int g = 0; g < kWRows / 8; ++g) {
       const int row = 8 * g + dr;
       b_off[g] = (uint32_t)((min(n0 + row, n - 1) - nb0) * k + ((ds ^ swz(row)) << 4));
     }
     const uint32_t s_off = (uint32_t)(min((int64_t)lane, m - 1) * nkb * 4);
     const uint32_t lds_ring = lds_addr(&ring[0]);
     auto issue = [&](int kb) {
-      const uint32_t slot = lds_ring + (uint32_t)((kb % kWideSlots) * sizeof(WideSlot<kAT>));
+      const uint32_t slot = lds_ring + (uint32_t)((kb % kWideSlots) * sizeof(WideSlot<kAT, kWT>));
       if (!bmover) {
 #pragma unroll
         for (int g = 0; g < kRows / 8; ++g) lds_dma16(a + (int64_t)kb * kBlock, a_off[g], slot + g * 1024);
-        if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + (kRows + kWideRows) * kBlock);
+        if (!kTab && lane < kRows) lds_dma4(a_s + kb, s_off, slot + (kRows + kWRows) * kBlock);
       } else {
 #pragma unroll
-        for (int g = 0; g < kWideRows / 8; ++g)
+        for (int g = 0; g < kWRows / 8; ++g)
           lds_dma16(b_base + (int64_t)kb * kBlock, b_off[g], slot + kRows * kBlock + g * 1024);
       }
     };
@@ -1166,10 +1170,10 @@ __global__ __launch_bounds__(64 * (kAT + 2)) void block_gemm_decode_wide_kernel(
   const int64_t nblk0 = min(n0 / kBlock, grid_n - 1);
   const float *bs0 = b_s + nblk0 * nkb;
   const float *bs1 = b_s + min(nblk0 + 1, grid_n - 1) * nkb;
-  f32x4 acc[kWideTiles];
+  f32x4 acc[kWT];
 #pragma unroll
-  for (int j = 0; j < kWideTiles; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x8 af[2], bf[2][kWideTiles];
+  for (int j = 0; j < kWT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  i32x8 af[2], bf[2][kWT];
   f32x4 sa[2];
   float sb0[2], sb1[2];
   auto frag = [&](const uint8_t *rows) {
@@ -1177,10 +1181,10 @@ __global__ __launch_bounds__(64 * (kAT + 2)) void block_gemm_decode_wide_kernel(
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
   auto read = [&](int kb, int buf) {   // kb may be nkb (a stale slot, never used)
-    const WideSlot<kAT> &sl = ring[kb % kWideSlots];
+    const WideSlot<kAT, kWT> &sl = ring[kb % kWideSlots];
     af[buf] = frag(&sl.a[wave * 16 * kBlock]);
 #pragma unroll
-    for (int j = 0; j < kWideTiles; ++j) bf[buf][j] = frag(&sl.b[j * 16 * kBlock]);
+    for (int j = 0; j < kWT; ++j) bf[buf][j] = frag(&sl.b[j * 16 * kBlock]);
     if (kTab) {
       const float *tb = &stab[(kb / kTabKb) & 1][((kb % kTabKb) >> 2) * 128 + (kb & 3)];
 #pragma unroll
@@ -1197,7 +1201,7 @@ __global__ __launch_bounds__(64 * (kAT + 2)) void block_gemm_decode_wide_kernel(
   };
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < kWideTiles; ++j) {
+    for (int j = 0; j < kWT; ++j) {
       const f32x4 p = mfma_e4m3_16x16x128(af[buf], bf[buf][j], f32x4{0.f, 0.f, 0.f, 0.f});
       // tile j's weight block: the workgroup's first, or the next one
       const float sb = (n0 + 16 * j) / kBlock == nblk0 ? sb0[buf] : sb1[buf];
@@ -1220,7 +1224,7 @@ __global__ __launch_bounds__(64 * (kAT + 2)) void block_gemm_decode_wide_kernel(
   if (nkb & 1) step(neven, 0);
 
 #pragma unroll
-  for (int j = 0; j < kWideTiles; ++j) {
+  for (int j = 0; j < kWT; ++j) {
     const int64_t col = n0 + 16 * j + fr;
     const float bv = col < n ? bias_at(bias, kBf16Out, col) : 0.0f;
 #pragma unroll
@@ -1465,10 +1469,10 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   // the decode kernels' A and weight transfers use 32-bit lane offsets (from
   // A's base, and from the first weight row of a wave or a workgroup)
   if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && kWideRows * k < ((int64_t)1 << 32)) {
-    const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows));
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
-    // the decode kernel's compute waves per workgroup: the fewest that keep
-    // its grid within one workgroup per CU (five if the CU count is unknown)
+    // the decode kernel's compute waves (the wide kernel's weight tiles) per
+    // workgroup: the fewest that keep the grid within one workgroup per CU
+    // (five if the CU count is unknown)
     const int64_t cus = current_device_cus();
     const int64_t want = cus > 0 ? (n + 16 * cus - 1) / (16 * cus) : kDecodeCompute;
     const int cw = want < 1 ? 1 : want > kDecodeCompute ? kDecodeCompute : (int)want;
@@ -1499,15 +1503,25 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   do {                                                                                                       \
     if (tab) FP8BSQ_DECODE_T(MT, true); else FP8BSQ_DECODE_T(MT, false);                                   \
   } while (0)
+#define FP8BSQ_WIDE_W(AT, TAB, WT)                                                                          \
+  do {                                                                                                       \
+    const dim3 block(64 * (AT + 2)), wgrid((unsigned)((n + 16 * (WT) - 1) / (16 * (WT))));                  \
+    if (c_bf16)                                                                                              \
+      hipLaunchKernelGGL((block_gemm_decode_wide_kernel<true, AT, TAB, WT>), wgrid, block, 0, stream, a, a_s, \
+                         b, b_s, c, m, n, k, bias);                                                          \
+    else                                                                                                     \
+      hipLaunchKernelGGL((block_gemm_decode_wide_kernel<false, AT, TAB, WT>), wgrid, block, 0, stream, a,    \
+                         a_s, b, b_s, c, m, n, k, bias);                                                     \
+  } while (0)
 #define FP8BSQ_WIDE_T(AT, TAB)                                                                              \
   do {                                                                                                       \
-    const dim3 block(64 * (AT + 2));                                                                         \
-    if (c_bf16)                                                                                              \
-      hipLaunchKernelGGL((block_gemm_decode_wide_kernel<true, AT, TAB>), grid, block, 0, stream, a, a_s, b,  \
-                         b_s, c, m, n, k, bias);                                                             \
-    else                                                                                                     \
-      hipLaunchKernelGGL((block_gemm_decode_wide_kernel<false, AT, TAB>), grid, block, 0, stream, a, a_s, b, \
-                         b_s, c, m, n, k, bias);                                                             \
+    switch (cw) {                                                                                            \
+      case 1: FP8BSQ_WIDE_W(AT, TAB, 1); break;                                                              \
+      case 2: FP8BSQ_WIDE_W(AT, TAB, 2); break;                                                              \
+      case 3: FP8BSQ_WIDE_W(AT, TAB, 3); break;                                                              \
+      case 4: FP8BSQ_WIDE_W(AT, TAB, 4); break;                                                              \
+      default: FP8BSQ_WIDE_W(AT, TAB, kWideTiles); break;                                                    \
+    }                                                                                                        \
   } while (0)
 #define FP8BSQ_WIDE(AT)                                                                                     \
   do {                                                                                                       \
@@ -1521,6 +1535,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
     }
 #undef FP8BSQ_WIDE
 #undef FP8BSQ_WIDE_T
+#undef FP8BSQ_WIDE_W
 #undef FP8BSQ_DECODE
 #undef FP8BSQ_DECODE_T
 #undef FP8BSQ_DECODE_W

@@ -1,12 +1,14 @@
-"""The decode kernel's workgroup width across weight widths.
+"""The decode kernels' workgroup width across weight widths.
 
 The decode kernel (M <= 32) launches one to five compute waves per workgroup,
-the fewest that keep its grid within one workgroup per CU: on a 256-CU device,
-one up to N = 4096, two up to 8192, three up to 12288, four up to 16384 and five
-above.  Cases sit on both sides of every boundary, with one and two activation
-row tiles (M <= 16, 17..32), K / 128 a multiple of 4 or not (scale table or
-per-block scales), both scale formats and both output dtypes, and must meet the
-oracle's bound on every element.  Inputs follow the GEMM recipe (normal
+and the wide decode kernel (32 < M <= 64) one to five weight tiles, the fewest
+that keep the grid within one workgroup per CU: on a 256-CU device, one up to
+N = 4096, two up to 8192, three up to 12288, four up to 16384 and five above.
+Cases sit on both sides of every boundary, with one and two activation row
+tiles (M <= 16, 17..32) and three and four in the wide kernel (33..48, 49..64),
+K / 128 a multiple of 4 or not (scale table or per-block scales), both scale
+formats and both output dtypes, and must meet the oracle's bound on every
+element.  Inputs follow the GEMM recipe (normal
 activations with outliers, E4M3 weight codes, log-uniform block scales).
 """
 
@@ -31,13 +33,19 @@ CASES = [  # m, n, k, scale_fmt, out
     (2, 12289, 512, "ue8m0", "f32"),
     (31, 16384, 512, "ue8m0", "bf16"),
     (8, 16385, 640, None, "f32"),
+    (33, 4096, 512, "ue8m0", "bf16"),
+    (48, 4097, 640, None, "f32"),
+    (64, 8193, 512, None, "bf16"),
+    (40, 12289, 640, "ue8m0", "f32"),
+    (64, 16384, 512, "ue8m0", "bf16"),
+    (49, 16385, 640, None, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("m,n,k,fmt,out", CASES)
 def test_decode_width(m, n, k, fmt, out):
     G.announce(f"decode width m={m} n={n} k={k} scale_fmt={fmt} out={out}")
-    d = gen.custom_gemm(seed=8000 + n, m=m, n=n, k=k, outliers=True)
+    d = gen.custom_gemm(seed=8000 + n + 100000 * m, m=m, n=n, k=k, outliers=True)
     dev = G.device()
     y, s = fb.act_quant(d["x"].to(dev), 128, fmt)
     w = torch.from_numpy(d["w"]).to(dev)
