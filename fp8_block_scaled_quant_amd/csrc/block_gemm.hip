@@ -609,8 +609,9 @@ __global__ __launch_bounds__(kThreads) void block_gemm_tile_kernel(
 // Fused act_quant (kFuseQ, M <= kFusedMaxM, bf16 activations): every
 // workgroup quantizes all of x [m, k] into LDS with act_quant's arithmetic,
 // and workgroup 0 also publishes the codes and scales; there is no mover and
-// no per-block barrier.  Eleven helper waves do the quantization while the
-// five compute waves already stream their weights: the helpers take x's
+// no per-block barrier.  Helper waves (the workgroup's sixteen waves less the
+// compute waves) do the quantization while the compute waves already stream
+// their weights: the helpers take x's
 // blocks in K order and count each finished block in LDS, and a compute wave
 // waits for a K block's count before it reads that block's codes.  The
 // compute waves do the same arithmetic in the same order as on the two-call
@@ -624,12 +625,13 @@ constexpr int kDecodeMaxKb = 160;
 // this many rows (one 16-row MFMA tile), within the code limits below: every
 // workgroup quantizes all of them, but on helper waves that overlap the
 // weight stream, so the redundant work stays off the critical path.  The
-// workgroup has kFusedWaves waves, four per SIMD: five compute waves and
-// eleven helpers.
+// workgroup has kFusedWaves waves, four per SIMD: the compute waves (one to
+// five, as the decode kernel chooses them for N) and helpers.  Fewer compute
+// waves per workgroup at narrow N measured 9-18% faster at N = 4096 and 7168
+// (M = 1-16), as the grid grows from 90 to 224 or 256 workgroups, even though
+// every workgroup repeats the quantization.
 constexpr int kFusedMaxM = 16;
 constexpr int kFusedWaves = 16;
-constexpr int kFusedCompute = 5;
-constexpr int kFusedHelpers = kFusedWaves - kFusedCompute;
 // Most bytes of codes the fused path keeps in LDS, beside the five weight
 // rings and the scales: 80 KB keeps the workgroup within 160 KB.  Up to that
 // many codes (m * k) all of x stays in LDS; beyond it, up to
@@ -657,13 +659,13 @@ __host__ __device__ constexpr int fused_ring_blocks(int m) {
 // workgroup-scope release; a reader that sees done[kb] == m with acquire sees
 // the whole K block.  With kRing, block kb's codes go to ring slot
 // kb & ring_mask, and a helper first waits until every compute wave has
-// finished reading the slot's previous block (prog[w]: K blocks wave w has
-// read).  Workgroup 0 also writes the codes and scales to a_q /
+// finished reading the slot's previous block (prog[w]: K blocks compute wave
+// w of kNC has read).  Workgroup 0 also writes the codes and scales to a_q /
 // a_s_out, bit-identical to fp8_act_quant.  The helpers start at a raised
 // wave priority for their first batch, whose blocks the compute waves wait
 // for first, and drop to the normal priority after it (measured: 2-4% faster
 // at M = 1-16 than either priority throughout).
-template <int kRows, int kThreadsQ, bool kRing, int kBatchQ = 4>
+template <int kRows, int kThreadsQ, bool kRing, int kNC, int kBatchQ = 4>
 __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int m, int nkb, int hq,
                                                 bool ue8m0, uint8_t *aq, float (*as_t)[kRows], int *done,
                                                 const int *prog, int ring_mask, uint8_t *__restrict__ a_q,
@@ -706,7 +708,7 @@ __device__ __forceinline__ void fused_act_quant(const u32x4 *__restrict__ x, int
           for (int spin = 0; spin < (1 << 20); ++spin) {
             int lo = __hip_atomic_load(&prog[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-            for (int w = 1; w < kFusedCompute; ++w)
+            for (int w = 1; w < kNC; ++w)
               lo = min(lo, __hip_atomic_load(&prog[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
             seen = lo;
             if (kb <= seen + ring_mask) break;
@@ -767,8 +769,7 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kCW + 1)) void bl
     const void *__restrict__ bias, bool ue8m0 = false, uint8_t *__restrict__ a_q = nullptr,
     float *__restrict__ a_s_out = nullptr) {
   static_assert(kCW >= 1 && kCW <= kDecodeCompute, "one to five compute waves");
-  static_assert(!kFuseQ || (kMT == 1 && kFusedMaxM <= 16 && kCW == kFusedCompute),
-                "the fused path: one 16-row tile, five compute waves and the helpers");
+  static_assert(!kFuseQ || (kMT == 1 && kFusedMaxM <= 16), "the fused path: one 16-row tile");
   static_assert(!kRing || kFuseQ, "the ring belongs to the fused path");
   static_assert(kMT <= 2, "up to 32 activation rows");
   constexpr int kRows = 16 * kMT;
@@ -884,7 +885,7 @@ __global__ __launch_bounds__(kFuseQ ? 64 * kFusedWaves : 64 * (kCW + 1)) void bl
     // the helper waves only quantize; the fused K loop has no barrier to miss
     if (wave >= kCW) {
       __builtin_amdgcn_s_setprio(3);
-      fused_act_quant<kRows, 64 * kFusedHelpers, kRing>((const u32x4 *)a, (int)m, nkb, t - 64 * kCW,
+      fused_act_quant<kRows, 64 * (kFusedWaves - kCW), kRing, kCW>((const u32x4 *)a, (int)m, nkb, t - 64 * kCW,
                                                         ue8m0, aq, as_t, q_done, q_prog, ring_mask, a_q, a_s_out,
                                                         blockIdx.x == 0);
       return;
@@ -1255,6 +1256,16 @@ static int current_device_cus() {
   return cus;
 }
 
+// Compute waves of the decode kernel and the fused path, or weight tiles of
+// the wide decode kernel, per workgroup for a weight of n rows: the fewest
+// (one to five) that keep the grid within one workgroup per CU; five if the
+// CU count is unknown.
+static int decode_width(int64_t n) {
+  const int64_t cus = current_device_cus();
+  const int64_t want = cus > 0 ? (n + 16 * cus - 1) / (16 * cus) : kDecodeCompute;
+  return want < 1 ? 1 : want > kDecodeCompute ? kDecodeCompute : (int)want;
+}
+
 // the tiled kernel serves m > 64 while A, B and a_s fit its 32-bit per-lane offsets
 static bool tiled_path(int64_t m, int64_t n, int64_t k) {
   return m > 64 && m * k < ((int64_t)1 << 32) && n * k < ((int64_t)1 << 32);
@@ -1470,12 +1481,7 @@ hipError_t launch_block_gemm(const uint8_t *a, const float *a_s, const uint8_t *
   // A's base, and from the first weight row of a wave or a workgroup)
   if (m <= kDecodeMaxM && m * k < ((int64_t)1 << 32) && kWideRows * k < ((int64_t)1 << 32)) {
     const bool tab = (k / kBlock) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
-    // the decode kernel's compute waves (the wide kernel's weight tiles) per
-    // workgroup: the fewest that keep the grid within one workgroup per CU
-    // (five if the CU count is unknown)
-    const int64_t cus = current_device_cus();
-    const int64_t want = cus > 0 ? (n + 16 * cus - 1) / (16 * cus) : kDecodeCompute;
-    const int cw = want < 1 ? 1 : want > kDecodeCompute ? kDecodeCompute : (int)want;
+    const int cw = decode_width(n);   // compute waves, or the wide kernel's weight tiles
     const dim3 dgrid((unsigned)((n + 16 * cw - 1) / (16 * cw)));
     // up to 32 rows: the decode kernel with MT activation row tiles per
     // compute wave; above: the wide kernel with AT row tiles, one per wave
@@ -1562,22 +1568,33 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
                                       int64_t m, int64_t n, int64_t k, uint8_t *a_q, float *a_s,
                                       hipStream_t stream) {
   // no mover: the compute waves, and the helpers that quantize x
-  const dim3 grid((unsigned)((n + kDecodeRows - 1) / kDecodeRows)), block(64 * kFusedWaves);
-  // all of x's codes in LDS, or (more of them) a ring of K blocks
-#define FP8BSQ_FUSED(RING, LDS)                                                                               \
+  const int cw = decode_width(n);
+  const dim3 grid((unsigned)((n + 16 * cw - 1) / (16 * cw))), block(64 * kFusedWaves);
+#define FP8BSQ_FUSED_W(RING, LDS, CW)                                                                         \
   do {                                                                                                         \
     if (c_bf16)                                                                                                \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecodeDepth, false, true, RING>), grid, block,     \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecodeDepth, false, true, RING, CW>), grid, block, \
                          (LDS), stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s); \
     else                                                                                                       \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecodeDepth, false, true, RING>), grid, block,    \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecodeDepth, false, true, RING, CW>), grid, block,\
                          (LDS), stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s); \
+  } while (0)
+#define FP8BSQ_FUSED(RING, LDS)                                                                               \
+  do {                                                                                                         \
+    switch (cw) {                                                                                              \
+      case 1: FP8BSQ_FUSED_W(RING, LDS, 1); break;                                                             \
+      case 2: FP8BSQ_FUSED_W(RING, LDS, 2); break;                                                             \
+      case 3: FP8BSQ_FUSED_W(RING, LDS, 3); break;                                                             \
+      case 4: FP8BSQ_FUSED_W(RING, LDS, 4); break;                                                             \
+      default: FP8BSQ_FUSED_W(RING, LDS, kDecodeCompute); break;                                               \
+    }                                                                                                          \
   } while (0)
   if (m * k <= kFusedMaxCodes)
     FP8BSQ_FUSED(false, (size_t)(m * k));
   else
     FP8BSQ_FUSED(true, (size_t)fused_ring_blocks((int)m) * m * kBlock);
 #undef FP8BSQ_FUSED
+#undef FP8BSQ_FUSED_W
   return hipGetLastError();
 }
 

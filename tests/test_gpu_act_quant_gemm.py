@@ -68,7 +68,8 @@ def test_ue8m0_and_fp32_out(m):
 # past 80 K at m = 5 and 16, m = 12 and 16 at K = 7168, m = 6 at K = 18432,
 # m = 5 at the longest K, and 120 K codes at m = 16.  Two kernels past the
 # limits: m = 16 with one more K block, m = 7 at K = 18432, m = 17, and K / 128
-# = 161.
+# = 161.  The weight widths take one to five compute waves per workgroup
+# (N = 4096 and below, 7168, 10000, 13000 and 18432 on a 256-CU device).
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 129, 128), (4, 17, 256), (2, 7168, 18432), (7, 500, 640),
                                    (1, 129, 128), (2, 96, 384), (4, 300, 20480), (5, 200, 1024),
                                    (5, 200, 16384), (5, 200, 16512), (6, 130, 1024), (8, 700, 2048),
@@ -76,7 +77,8 @@ def test_ue8m0_and_fp32_out(m):
                                    (13, 7168, 6144), (14, 129, 128), (15, 640, 2560), (16, 520, 5120),
                                    (16, 130, 5248), (16, 96, 128), (17, 200, 1024), (12, 700, 7168),
                                    (16, 700, 7168), (6, 300, 18432), (5, 640, 20480), (16, 130, 7680),
-                                   (16, 130, 7808), (7, 96, 18432), (2, 96, 20608)])
+                                   (16, 130, 7808), (7, 96, 18432), (2, 96, 20608), (4, 10000, 1024),
+                                   (9, 13000, 2048), (16, 12289, 7168)])
 def test_shapes(m, n, k):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
     _run(d["x"], d["w"], d["w_s"], None, "bf16", "shape")
