@@ -737,6 +737,11 @@ constexpr int kDecodeCompute = 5;                // most compute waves per workg
 constexpr int kDecodeRows = 16 * kDecodeCompute;   // weight rows per workgroup at that width
 constexpr int kDecodeLead = 6;                   // K blocks of A in flight ahead of use (ring: one more slot)
 constexpr int kDecodeDepth = 6;                  // weight ring depth per compute wave
+// The fused path at one or two compute waves per workgroup (narrow N) keeps
+// more weight blocks in flight per wave: 10 measured 3-5% faster than 6 at
+// N = 7168 (M = 1-4), and 14 no better.  The decode kernel, whose waves also
+// meet once per K block at the mover's barrier, measured 2-5% slower with it.
+constexpr int kFusedNarrowDepth = 10;
 
 template <int kMT>
 struct DecodeSlot {
@@ -1570,23 +1575,23 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
   // no mover: the compute waves, and the helpers that quantize x
   const int cw = decode_width(n);
   const dim3 grid((unsigned)((n + 16 * cw - 1) / (16 * cw))), block(64 * kFusedWaves);
-#define FP8BSQ_FUSED_W(RING, LDS, CW)                                                                         \
+#define FP8BSQ_FUSED_W(RING, LDS, CW, DEPTH)                                                                  \
   do {                                                                                                         \
     if (c_bf16)                                                                                                \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, kDecodeDepth, false, true, RING, CW>), grid, block, \
+      hipLaunchKernelGGL((block_gemm_decode_kernel<true, 1, DEPTH, false, true, RING, CW>), grid, block,        \
                          (LDS), stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s); \
     else                                                                                                       \
-      hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, kDecodeDepth, false, true, RING, CW>), grid, block,\
+      hipLaunchKernelGGL((block_gemm_decode_kernel<false, 1, DEPTH, false, true, RING, CW>), grid, block,       \
                          (LDS), stream, (const uint8_t *)x, nullptr, b, b_s, c, m, n, k, bias, ue8m0, a_q, a_s); \
   } while (0)
 #define FP8BSQ_FUSED(RING, LDS)                                                                               \
   do {                                                                                                         \
     switch (cw) {                                                                                              \
-      case 1: FP8BSQ_FUSED_W(RING, LDS, 1); break;                                                             \
-      case 2: FP8BSQ_FUSED_W(RING, LDS, 2); break;                                                             \
-      case 3: FP8BSQ_FUSED_W(RING, LDS, 3); break;                                                             \
-      case 4: FP8BSQ_FUSED_W(RING, LDS, 4); break;                                                             \
-      default: FP8BSQ_FUSED_W(RING, LDS, kDecodeCompute); break;                                               \
+      case 1: FP8BSQ_FUSED_W(RING, LDS, 1, kFusedNarrowDepth); break;                                          \
+      case 2: FP8BSQ_FUSED_W(RING, LDS, 2, kFusedNarrowDepth); break;                                          \
+      case 3: FP8BSQ_FUSED_W(RING, LDS, 3, kDecodeDepth); break;                                               \
+      case 4: FP8BSQ_FUSED_W(RING, LDS, 4, kDecodeDepth); break;                                               \
+      default: FP8BSQ_FUSED_W(RING, LDS, kDecodeCompute, kDecodeDepth); break;                                 \
     }                                                                                                          \
   } while (0)
   if (m * k <= kFusedMaxCodes)
