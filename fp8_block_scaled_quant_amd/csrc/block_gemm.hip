@@ -638,9 +638,11 @@ constexpr int kFusedWaves = 16;
 // kFusedRingMaxCodes, the codes go through a ring of fused_ring_blocks(m) K
 // blocks that the helpers refill as the compute waves finish reading them.
 // Past that limit the redundant quantization outweighs the saved kernel
-// boundary (measured at N = 7168, K = 18432: 8% slower at m = 12, 18% at 16).
+// boundary (measured against the two kernels: m = 16 at K = 7168 (112 K codes)
+// 7-12% slower at N = 4096-12288, m = 6 at K = 18432 (108 K) 9% slower at
+// N = 7168).
 constexpr int64_t kFusedMaxCodes = 80 * 1024;
-constexpr int64_t kFusedRingMaxCodes = 120 * 1024;
+constexpr int64_t kFusedRingMaxCodes = 96 * 1024;
 // K blocks of m rows' codes in the ring: the largest power of two that fits.
 __host__ __device__ constexpr int fused_ring_blocks(int m) {
   int r = 1;

@@ -285,7 +285,7 @@ FP8BSQ_API int fp8_block_gemm_split_noalloc(const uint8_t *a, const float *a_s, 
  *     (a_q, a_s) = fp8_act_quant(x, scale_fmt);
  *     c          = fp8_block_gemm(a_q, a_s, b, b_s)  (+ bias)
  * with outputs bit-identical to those two calls when bias is null.  For bf16 x with m <= 16,
- * k <= 20480 and m * k <= 122880 (the decode case) both happen in one kernel: in every workgroup helper
+ * k <= 20480 and m * k <= 98304 (the decode case) both happen in one kernel: in every workgroup helper
  * waves quantize x into LDS while the GEMM's waves stream the weight, and workgroup 0 also
  * writes a_q and a_s.  Otherwise
  * the two kernels are queued back to back on hip_stream (with

@@ -116,9 +116,9 @@ hipError_t launch_act_quant_gemm_fused(const void *x, bool ue8m0, const uint8_t 
   return result();
 }
 
-// the stand-in fuses bf16 activations of up to 16 rows and 120 K codes
+// the stand-in fuses bf16 activations of up to 16 rows and 96 K codes
 bool act_quant_gemm_fusable(bool x_bf16, int64_t m, int64_t k) {
-  return x_bf16 && m <= 16 && k > 0 && k <= 20480 && m * k <= 122880;
+  return x_bf16 && m <= 16 && k > 0 && k <= 20480 && m * k <= 98304;
 }
 
 }  // namespace fp8bsq

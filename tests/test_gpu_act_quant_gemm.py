@@ -1,6 +1,6 @@
 """GPU parity for fp8_act_quant_gemm (act_quant then the block GEMM, one call).
 
-For bf16 activations with m <= 16 (and m * k <= 120 K codes) the whole computation runs in
+For bf16 activations with m <= 16 (and m * k <= 96 K codes) the whole computation runs in
 one kernel (helper waves quantize x while the GEMM's waves stream the weight; past 80 K codes
 through an LDS ring of K blocks); larger m and fp32 activations queue the two kernels.
 Every case checks:
@@ -11,8 +11,8 @@ Every case checks:
   arithmetic;
 * C is within the oracle GEMM's bound (1e-3 * sum |a b|, + 1 bf16 ulp).
 
-Cases: the decode workloads M = 1-4, 8, 11 (fused), 12, 16 (fused through the
-ring) and 64 (two kernels), both scale formats, fp32 output, ragged N, a single
+Cases: the decode workloads M = 1-4, 8, 11 (fused), 12 (fused through the ring)
+and 16, 64 (two kernels), both scale formats, fp32 output, ragged N, a single
 K block, the long-K decode shape (K = 18432), the longest K the fused path takes
 (K / 128 = 160), the most rows it takes (16), the limits of the LDS-resident and
 the ring forms, fp32 activations, and the Python binding.
@@ -64,11 +64,11 @@ def test_ue8m0_and_fp32_out(m):
 # (k = 128) and three; a last batch of four loads per lane that is only partly
 # used (k = 18432, m = 2: 288 blocks for 44 sixteen-lane helper groups x 4);
 # the longest K, at m = 4; 80 K codes at m = 5 and m = 16; every row count in
-# between at a few K.  Through the ring (80 K < m * k <= 120 K): one K block
-# past 80 K at m = 5 and 16, m = 12 and 16 at K = 7168, m = 6 at K = 18432,
-# m = 5 at the longest K, and 120 K codes at m = 16.  Two kernels past the
-# limits: m = 16 with one more K block, m = 7 at K = 18432, m = 17, and K / 128
-# = 161.  The weight widths take one to five compute waves per workgroup
+# between at a few K.  Through the ring (80 K < m * k <= 96 K): one K block
+# past 80 K at m = 5 and 16, m = 12 and 13 at K = 7168, m = 5 at K = 19200,
+# and 96 K codes at m = 16.  Two kernels past the limits: m = 16 with one more
+# K block, m = 16 at K = 7168, m = 6 and 7 at K = 18432, m = 5 at the longest
+# K, m = 17, and K / 128 = 161.  The weight widths take one to five compute waves per workgroup
 # (N = 4096 and below, 7168, 10000, 13000 and 18432 on a 256-CU device).
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (3, 129, 128), (4, 17, 256), (2, 7168, 18432), (7, 500, 640),
                                    (1, 129, 128), (2, 96, 384), (4, 300, 20480), (5, 200, 1024),
@@ -76,9 +76,9 @@ def test_ue8m0_and_fp32_out(m):
                                    (9, 257, 4096), (10, 96, 384), (11, 300, 7168), (12, 300, 7168),
                                    (13, 7168, 6144), (14, 129, 128), (15, 640, 2560), (16, 520, 5120),
                                    (16, 130, 5248), (16, 96, 128), (17, 200, 1024), (12, 700, 7168),
-                                   (16, 700, 7168), (6, 300, 18432), (5, 640, 20480), (16, 130, 7680),
-                                   (16, 130, 7808), (7, 96, 18432), (2, 96, 20608), (4, 10000, 1024),
-                                   (9, 13000, 2048), (16, 12289, 7168)])
+                                   (16, 700, 7168), (6, 300, 18432), (5, 640, 20480), (16, 130, 6144),
+                                   (16, 130, 6272), (7, 96, 18432), (2, 96, 20608), (4, 10000, 1024),
+                                   (9, 13000, 2048), (13, 12289, 7168), (5, 640, 19200)])
 def test_shapes(m, n, k):
     d = gen.custom_gemm(seed=m * 1000 + n + k, m=m, n=n, k=k, outliers=True)
     _run(d["x"], d["w"], d["w_s"], None, "bf16", "shape")

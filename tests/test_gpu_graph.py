@@ -22,10 +22,10 @@ pytestmark = pytest.mark.gpu
 
 
 # M = 1 and 8: act_quant fused into the decode GEMM (one kernel, helper waves
-# and LDS counters); M = 16: the same through the LDS ring; M = 20: act_quant
+# and LDS counters); M = 12: the same through the LDS ring; M = 20: act_quant
 # then the decode GEMM; M = 300: act_quant then the tiled GEMM.
 @pytest.mark.parametrize("m,n,k,scale_fmt", [(1, 18432, 7168, None), (8, 18432, 7168, None),
-                                             (16, 18432, 7168, None), (20, 18432, 7168, None),
+                                             (12, 18432, 7168, None), (20, 18432, 7168, None),
                                              (300, 2304, 1024, "ue8m0")])
 def test_step_replays_match_eager(m, n, k, scale_fmt):
     dev = G.device()

@@ -7,7 +7,7 @@ block must still match the oracle bit for bit, and the canary bands around
 every output must be untouched.  Checked for bf16 and fp32 activations, both
 scale formats, and for the one-kernel act_quant_gemm path (m <= 16), whose
 helper waves quantize x in every workgroup (with all of x in LDS, and through
-the LDS ring at m = 16, k = 7168).
+the LDS ring at m = 12, k = 7168).
 """
 
 import numpy as np
@@ -65,7 +65,7 @@ def test_act_quant_confines_non_finite_blocks(dtype, fmt):
     assert np.array_equal(codes[cb], wq[cb])
 
 
-@pytest.mark.parametrize("m,k", [(1, 2048), (5, 2048), (16, 2048), (16, 7168)])
+@pytest.mark.parametrize("m,k", [(1, 2048), (5, 2048), (16, 2048), (12, 7168)])
 def test_fused_act_quant_gemm_confines_non_finite_blocks(m, k):
     d = gen.custom_gemm(seed=93 + m, m=m, n=700, k=k)
     x = d["x"]
